@@ -1,0 +1,241 @@
+"""Benchmark of the W8A8 per-channel prefill layer on one MI355X.
+
+One step = the whole hot path of the layer on one batch: online per-token
+activation quantization (quantize_act) followed by the int8 GEMM with int32
+accumulation and the fp16 rescale epilogue (w8a8_gemm_pc) -- the two launches
+linear() makes for M > 1 -- at M=4096, N=10240, K=2560 with outlier-laden
+synthetic activations.  Inputs are resident in HBM before timing starts; the
+offline weight quantization is done once, outside the timed region.
+
+Prints one JSON line:  value = 2*M*N*K / step time (TOPS, act-quant included),
+roofline = the GEMM kernel's own rate against the dense int8 MFMA peak (from
+HIP events around each GEMM launch in the timed loop), cpu_baseline = the CPU
+oracle timed on a bounded sample of rows of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --copy-probe      # plain copy kernel, for HBM counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA (published), in tera-ops/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
+# The pages' figure for this exact workload (per-channel W8A8, N=10240, K=2560,
+# M=4096): 4.41 ms on Apple M5 Pro, i.e. 2*M*N*K / 4.41 ms = 48.7 TOPS.  Another
+# machine: context only.
+PAGES_TOPS_M5PRO = 2 * 4096 * 10240 * 2560 / 4.41e-3 / 1e12
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_pc_headline_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "w4a8_int8_gemm_amd", "csrc", "gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain copy of known size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def gemm_source_hash() -> str:
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(per_launch_bytes_alg: float):
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or None
+    if there are none or the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_probe():
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy probe: 5 copies of {n} bytes")
+
+
+def cpu_baseline(x, wt_q, sw, M, N, K, target_s):
+    """The oracle (untuned) on the first `rows` tokens of the same workload."""
+    import oracle
+    import numpy as np
+
+    def run(rows):
+        t0 = time.perf_counter()
+        r = oracle.w8a8_pc(x[:rows], wt_q, sw)
+        dt = time.perf_counter() - t0
+        assert r["y"].shape == (rows, N)
+        return dt
+
+    rows = 8
+    dt = run(rows)
+    while dt < 0.5 and rows < M:
+        rows = min(M, rows * 4)
+        dt = run(rows)
+    if dt < target_s and rows < M:
+        rows = int(min(M, max(rows, rows * target_s / max(dt, 1e-6))))
+        dt = run(rows)
+    tops = 2.0 * rows * N * K / dt / 1e12
+    return {"value": round(tops, 6), "unit": "TOPS", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"first {rows} of {M} tokens (all N={N}, K={K}): quantize, int32 GEMM, "
+                      f"fp64 rescale, same inputs as the GPU run"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the design notes describe how the layer would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a8_int8_gemm_amd as w
+
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if not w.is_available():
+        raise SystemExit("cuda:0 is not gfx950: " + w.lib().w4a8_last_error().decode())
+
+    M, N, K = 4096, 10240, 2560
+    log(f"workload: W8A8 per-channel M={M} N={N} K={K}, outlier activations, seed 0")
+    x = synth.activations(M, K, seed=0, outliers=True)
+    wt = synth.weights(N, K, seed=0)
+    xd = torch.from_numpy(x).cuda()
+    wd = torch.from_numpy(wt).cuda()
+    wq, sw = w.quantize_weight_int8(wd)          # offline step
+    del wd
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        w.quantize_act(xd, 0, out=xq, scale=xs)
+        w.w8a8_gemm_pc(xq, xs, wq, sw, out=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        ev[i][0].record(stream)
+        w.quantize_act(xd, 0, out=xq, scale=xs)
+        ev[i][1].record(stream)
+        w.w8a8_gemm_pc(xq, xs, wq, sw, out=y)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    q_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K_steps)])
+    g_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K_steps)])
+    ms_per_step = wall * 1e3 / K_steps
+    ops = 2.0 * M * N * K
+    value = ops / (ms_per_step * 1e-3) / 1e12
+
+    # linear() on the same inputs: same two launches, checked for identical output
+    ws = torch.empty((w.linear_workspace_size(w.Mode.W8A8_PC, M, K),), dtype=torch.uint8,
+                     device="cuda")
+    y_lin = torch.empty_like(y)
+    w.linear(w.Mode.W8A8_PC, xd, wq, sw, workspace=ws, out=y_lin)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y_lin, y))
+    t1 = time.perf_counter()
+    for _ in range(K_steps):
+        w.linear(w.Mode.W8A8_PC, xd, wq, sw, workspace=ws, out=y_lin)
+    torch.cuda.synchronize()
+    linear_ms = (time.perf_counter() - t1) * 1e3 / K_steps
+
+    gemm_ms = float(g_ms.mean())
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    quant_ms = float(q_ms.mean())
+    quant_bytes = M * K * 2 + M * K + M * 4            # read fp16 x, write int8 codes + scales
+    gemm_bytes_alg = M * K + N * K + M * N * 2 + (M + N) * 4
+    traffic = traffic_from_profiles(gemm_bytes_alg)
+
+    out = {
+        "metric": "W8A8 prefill TOPS incl. act-quant, N=10240 K=2560 M=4096; % int8 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_TOPS_M5PRO, 3),
+        "vs_baseline_note": "pages' figure for this workload on Apple M5 Pro "
+                            "(4.41 ms = 48.7 TOPS); another machine, context only",
+        "pct_int8_peak": round(100.0 * value / PEAK_INT8_TOPS, 2),
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "w8a8 per-channel prefill, M=4096 N=10240 K=2560, "
+                               "N(0,1) activations with 8 outlier channels x50 and 1% tokens x20, "
+                               "N(0,0.02) weights, seed 0",
+                   "M": M, "N": N, "K": K, "mode": "W8A8_PC", "group_size": 0},
+        "roofline": {"kernel": "w8a8_gemm_pc", "bound": "mfma", "achieved": round(gemm_tops, 2),
+                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                     "avg_launch_us": round(gemm_ms * 1e3, 2),
+                     "algorithmic_bytes": gemm_bytes_alg},
+        "quantize_act": {"avg_launch_us": round(quant_ms * 1e3, 2),
+                         "achieved_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                         "peak_GBps": PEAK_HBM_GBS,
+                         "frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "linear_ms_per_step": round(linear_ms, 5),
+        "linear_matches_kernels": same,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the oracle on a sample of the same workload ...")
+        import oracle
+        owq, osw = oracle.quantize_weight_int8(wt)
+        out["cpu_baseline"] = cpu_baseline(x, owq, osw, M, N, K, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

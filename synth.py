@@ -48,6 +48,30 @@ def weights(N: int, K: int, seed: int = 0, layer: int = 0, sigma: float = 0.02) 
     return w.astype(np.float16)
 
 
+def int8_codes(rows: int, K: int, seed: int = 0, salt: int = 0) -> np.ndarray:
+    """int8 ``[rows, K]`` in [-127, 127], bell-shaped like quantized normal data,
+    with the extreme codes present in every row."""
+    rng = np.random.default_rng([seed, 4, salt])
+    c = np.clip(np.rint(rng.standard_normal((rows, K)) * 42.0), -127, 127).astype(np.int8)
+    if K >= 2:
+        c[:, rng.integers(0, K)] = 127
+        c[:, rng.integers(0, K)] = -127
+    return c
+
+
+def packed_int4(rows: int, K: int, seed: int = 0, salt: int = 0) -> np.ndarray:
+    """uint8 ``[rows, K/2]``: random bytes, i.e. every nibble value including 0x8."""
+    rng = np.random.default_rng([seed, 5, salt])
+    return rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+
+
+def scales(rows: int, groups: int = 0, seed: int = 0, salt: int = 0, magnitude: float = 0.02) -> np.ndarray:
+    """Positive fp32 scales ``[rows]`` (groups == 0) or ``[rows, groups]``."""
+    rng = np.random.default_rng([seed, 6, salt])
+    shape = (rows,) if groups == 0 else (rows, groups)
+    return (rng.uniform(0.25, 4.0, size=shape) * magnitude / 127.0).astype(np.float32)
+
+
 def sample_indices(n: int, count: int, seed: int = 0, salt: int = 0) -> np.ndarray:
     """Sorted distinct indices in ``[0, n)`` that always include the first and last index."""
     rng = np.random.default_rng([seed, 7, salt])

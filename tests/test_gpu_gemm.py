@@ -1,0 +1,120 @@
+"""GPU parity of the int8 GEMMs: raw int32 sums and per-group partials bit for
+bit, fp16 outputs within tolerance, against the oracle on the same seeded
+int8 codes and scales (drawn by the input generator, not by either side).
+
+Shapes are chosen to exercise every tile configuration the library selects
+(64x64, 128x64, 128x128, 256x128, 256x160), ragged M/N edges, N not a multiple
+of 4 (scalar stores), and K with a half-filled last stage (K % 128 == 64)."""
+import numpy as np
+import pytest
+
+import synth
+from tests.parity_util import assert_equal, assert_fp16_close, dev, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    return require_gpu()
+
+
+# (M, N, K): covers 64x64 (M<=64), 128x64, 128x128, 256x128, 256x160 selections
+PC_SHAPES = [
+    (16, 512, 256), (1, 96, 64), (3, 100, 192), (64, 64, 64),
+    (65, 130, 320), (200, 300, 192), (257, 321, 256),
+    (1024, 4096, 128), (2048, 8192, 128), (2048, 10240, 128), (1500, 10240, 192),
+]
+
+
+@pytest.mark.parametrize("M,N,K", PC_SHAPES)
+def test_gemm_i32_and_pc(torch_gpu, oracle, M, N, K):
+    import w4a8_int8_gemm_amd as w
+    print(f"gemm pc M={M} N={N} K={K}", flush=True)
+    seed = M + N + K
+    xq, wq = synth.int8_codes(M, K, seed, 0), synth.int8_codes(N, K, seed, 1)
+    sa, sw = synth.scales(M, 0, seed, 0, 3.0), synth.scales(N, 0, seed, 1)
+    c_ref = oracle.gemm_i32(xq, wq)
+    y_ref = oracle.epilogue_pc(c_ref, sa, sw)
+    c = w.w8a8_gemm_i32(dev(xq), dev(wq))
+    assert_equal(host(c), c_ref, "int32 sums")
+    y = w.w8a8_gemm_pc(dev(xq), dev(sa), dev(wq), dev(sw))
+    assert_fp16_close(host(y), y_ref, what="fp16 y")
+
+
+PG_SHAPES = [(16, 512, 256), (3, 100, 384), (200, 300, 640), (257, 321, 512),
+             (1024, 4096, 256), (2048, 8192, 256)]
+
+
+@pytest.mark.parametrize("gs", [64, 128])
+@pytest.mark.parametrize("M,N,K", PG_SHAPES)
+def test_gemm_pg(torch_gpu, oracle, M, N, K, gs):
+    import w4a8_int8_gemm_amd as w
+    print(f"gemm pg M={M} N={N} K={K} gs={gs}", flush=True)
+    seed = M * 3 + N + K + gs
+    G = K // gs
+    xq, wq = synth.int8_codes(M, K, seed, 0), synth.int8_codes(N, K, seed, 1)
+    sa, sw = synth.scales(M, G, seed, 0, 3.0), synth.scales(N, G, seed, 1)
+    p_ref = oracle.gemm_partials(xq, wq, gs)
+    y_ref, t_ref = oracle.epilogue_pg(p_ref, sa, sw)
+    p = w.w8a8_gemm_pg_partials(dev(xq), dev(wq), gs)
+    assert_equal(host(p), p_ref, "per-group partials")
+    y = w.w8a8_gemm_pg(dev(xq), dev(sa), dev(wq), dev(sw), gs)
+    assert_fp16_close(host(y), y_ref, t_ref, G, what="fp16 y")
+
+
+@pytest.mark.parametrize("gs", [64, 128])
+@pytest.mark.parametrize("M,N,K", PG_SHAPES)
+def test_gemm_w4a8(torch_gpu, oracle, M, N, K, gs):
+    import w4a8_int8_gemm_amd as w
+    print(f"gemm w4a8 M={M} N={N} K={K} gs={gs}", flush=True)
+    seed = M * 5 + N + K + gs
+    G = K // gs
+    xq, w4 = synth.int8_codes(M, K, seed, 0), synth.packed_int4(N, K, seed, 1)
+    sa, sw = synth.scales(M, 0, seed, 0, 3.0), synth.scales(N, G, seed, 1, 0.3)
+    p_ref = oracle.gemm_partials(xq, oracle.unpack_int4(w4, K), gs)
+    y_ref, t_ref = oracle.epilogue_w4a8(p_ref, sa, sw)
+    p = w.w4a8_gemm_partials(dev(xq), dev(w4), gs)
+    assert_equal(host(p), p_ref, "per-group partials")
+    y = w.w4a8_gemm(dev(xq), dev(sa), dev(w4), dev(sw), gs)
+    assert_fp16_close(host(y), y_ref, t_ref, G, what="fp16 y")
+
+
+def test_int4_every_nibble(torch_gpu, oracle):
+    """Rows of 0x88 (two -8 codes, which the quantizer never emits) and 0x77."""
+    import w4a8_int8_gemm_amd as w
+    M, N, K, gs = 64, 64, 256, 128
+    w4 = synth.packed_int4(N, K, 1)
+    w4[0, :] = 0x88
+    w4[1, :] = 0x77
+    xq = synth.int8_codes(M, K, 1)
+    xq[0, :] = -127
+    p_ref = oracle.gemm_partials(xq, oracle.unpack_int4(w4, K), gs)
+    assert_equal(host(w.w4a8_gemm_partials(dev(xq), dev(w4), gs)), p_ref, "partials")
+
+
+def test_extreme_int8_codes(torch_gpu, oracle):
+    """All +-127 codes at K = 16384: sums reach 127^2 * K."""
+    import w4a8_int8_gemm_amd as w
+    M, N, K = 64, 64, 16384
+    xq = np.full((M, K), 127, np.int8)
+    xq[1::2] = -127
+    wq = np.full((N, K), 127, np.int8)
+    wq[::3] = -127
+    c_ref = oracle.gemm_i32(xq, wq)
+    assert int(np.abs(c_ref).max()) == 127 * 127 * K
+    assert_equal(host(w.w8a8_gemm_i32(dev(xq), dev(wq))), c_ref, "int32 sums")
+
+
+def test_zero_rows_and_empty(torch_gpu):
+    import torch
+    import w4a8_int8_gemm_amd as w
+    M, N, K = 70, 96, 256
+    xq, wq = synth.int8_codes(M, K, 1), synth.int8_codes(N, K, 2)
+    xq[5] = 0
+    sa, sw = synth.scales(M, 0, 1), synth.scales(N, 0, 2)
+    y = host(w.w8a8_gemm_pc(dev(xq), dev(sa), dev(wq), dev(sw)))
+    assert np.all(y[5] == 0)
+    e = torch.empty((0, K), dtype=torch.int8, device="cuda")
+    out = w.w8a8_gemm_pc(e, torch.empty((0,), dtype=torch.float32, device="cuda"), dev(wq), dev(sw))
+    assert out.shape == (0, N)

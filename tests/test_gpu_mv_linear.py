@@ -1,0 +1,105 @@
+"""GPU parity of the decode matrix-vector kernel and of linear()'s path
+selection, each side running its own whole pipeline from the fp16 sources."""
+import numpy as np
+import pytest
+
+import synth
+from tests.parity_util import assert_equal, assert_fp16_close, dev, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    return require_gpu()
+
+
+@pytest.mark.parametrize("N,K", [(10240, 2560), (512, 256), (100, 16), (333, 4096),
+                                 (64, 14336), (257, 4112), (7, 32768)])
+def test_int8_mv(torch_gpu, oracle, N, K):
+    import w4a8_int8_gemm_amd as w
+    print(f"int8_mv N={N} K={K}", flush=True)
+    x = synth.activations(1, K, seed=K, outliers=True)
+    wt = synth.weights(N, K, seed=N)
+    wq, sw = oracle.quantize_weight_int8(wt)
+    r = oracle.int8_mv(x, wq, sw)
+    y, xq, xs = w.int8_mv(dev(x[0]), dev(wq), dev(sw), return_codes=True)
+    assert_equal(host(xs), r["sa"], "token scale")
+    assert_equal(host(xq), r["xq"][0], "token codes")
+    assert_fp16_close(host(y), r["y"][0], what="fp16 y")
+    # bit-identical to the GEMM path at M = 1
+    xq2, xs2 = w.quantize_act(dev(x))
+    y2 = w.w8a8_gemm_pc(xq2, xs2, dev(wq), dev(sw))
+    assert_equal(host(y), host(y2)[0], "MV vs GEMM at M=1")
+
+
+def test_int8_mv_zero_token(torch_gpu, oracle):
+    import w4a8_int8_gemm_amd as w
+    x = np.zeros((2560,), np.float16)
+    wq, sw = oracle.quantize_weight_int8(synth.weights(64, 2560))
+    y, xq, xs = w.int8_mv(dev(x), dev(wq), dev(sw), return_codes=True)
+    assert np.all(host(y) == 0) and np.all(host(xq) == 0) and host(xs)[0] == 0
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 64, 300])
+def test_linear_pc_end_to_end(torch_gpu, oracle, M):
+    """GPU: quantize_weight_int8 + linear.  Oracle: its own quantizer + GEMM."""
+    import w4a8_int8_gemm_amd as w
+    N, K = 384, 512
+    x = synth.activations(M, K, seed=M, outliers=True)
+    wt = synth.weights(N, K, seed=7)
+    wq_g, sw_g = w.quantize_weight_int8(dev(wt))
+    wq, sw = oracle.quantize_weight_int8(wt)
+    assert_equal(host(wq_g), wq, "weight codes")
+    assert_equal(host(sw_g), sw, "weight scales")
+    r = oracle.linear("pc", x, wq, sw)
+    y = w.linear(w.Mode.W8A8_PC, dev(x), wq_g, sw_g)
+    assert_fp16_close(host(y), r["y"], what=f"linear pc M={M}")
+    if M == 1:   # the dispatch picked the MV kernel: identical to calling it directly
+        assert_equal(host(y)[0], host(w.int8_mv(dev(x[0]), wq_g, sw_g)), "dispatch to MV")
+    else:        # identical to quantize_act + w8a8_gemm_pc
+        xq, xs = w.quantize_act(dev(x))
+        assert_equal(host(y), host(w.w8a8_gemm_pc(xq, xs, wq_g, sw_g)), "dispatch to GEMM")
+
+
+@pytest.mark.parametrize("gs", [64, 128])
+@pytest.mark.parametrize("M", [1, 3, 130])
+def test_linear_pg_end_to_end(torch_gpu, oracle, M, gs):
+    import w4a8_int8_gemm_amd as w
+    N, K = 200, 1024
+    x = synth.activations(M, K, seed=M + gs, outliers=True)
+    wt = synth.weights(N, K, seed=8)
+    wq_g, sw_g = w.quantize_weight_int8(dev(wt), gs)
+    wq, sw = oracle.quantize_weight_int8(wt, gs)
+    assert_equal(host(wq_g), wq, "weight codes")
+    r = oracle.linear("pg", x, wq, sw, gs)
+    y = w.linear(w.Mode.W8A8_PG, dev(x), wq_g, sw_g, gs)
+    assert_fp16_close(host(y), r["y"], r["t"], K // gs, what=f"linear pg M={M}")
+
+
+@pytest.mark.parametrize("gs", [64, 128])
+@pytest.mark.parametrize("M", [1, 3, 130])
+def test_linear_w4a8_end_to_end(torch_gpu, oracle, M, gs):
+    import w4a8_int8_gemm_amd as w
+    N, K = 200, 1024
+    x = synth.activations(M, K, seed=M + 2 * gs, outliers=True)
+    wt = synth.weights(N, K, seed=9)
+    w4_g, s4_g = w.pack_weight_int4(dev(wt), gs)
+    w4, s4 = oracle.pack_weight_int4(wt, gs)
+    assert_equal(host(w4_g), w4, "packed weights")
+    assert_equal(host(s4_g), s4, "int4 scales")
+    r = oracle.linear("w4a8", x, w4, s4, gs)
+    y = w.linear(w.Mode.W4A8, dev(x), w4_g, s4_g, gs)
+    assert_fp16_close(host(y), r["y"], r["t"], K // gs, what=f"linear w4a8 M={M}")
+
+
+def test_linear_workspace_checks(torch_gpu):
+    import torch
+    import w4a8_int8_gemm_amd as w
+    x = dev(synth.activations(8, 256))
+    wq = torch.zeros((16, 256), dtype=torch.int8, device="cuda")
+    sw = torch.ones((16,), dtype=torch.float32, device="cuda")
+    small = torch.empty((64,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(w.W4A8Error) as e:
+        w.linear(w.Mode.W8A8_PC, x, wq, sw, workspace=small)
+    assert e.value.status == w.Status.ERR_WORKSPACE

@@ -1,0 +1,77 @@
+"""The GPU kernels' quantizer fast path (multiply by fl32(1/s), guard near
+rounding boundaries, division rule for guarded elements) compiled for the
+host and checked against the oracle on every fp16 input for many scales."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "native", "quant_rule_shim.cpp")
+
+
+@pytest.fixture(scope="module")
+def shim(tmp_path_factory):
+    so = str(tmp_path_factory.mktemp("shim") / "quant_rule_shim.so")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-fno-fast-math",
+                    "-ffp-contract=off", SRC, "-o", so, "-lm"], check=True)
+    L = ctypes.CDLL(so)
+    fp = ctypes.POINTER(ctypes.c_float)
+    i8p = ctypes.POINTER(ctypes.c_int8)
+    L.shim_quantize.argtypes = [fp, ctypes.c_int, ctypes.c_float, ctypes.c_float, i8p, fp]
+    L.shim_quantize.restype = ctypes.c_int
+    L.shim_fast_only.argtypes = [fp, ctypes.c_int, ctypes.c_float, ctypes.c_float, i8p]
+    return L
+
+
+def _run(shim, xs16: np.ndarray, amax16, qmax):
+    x = xs16.astype(np.float32)
+    q = np.empty(x.shape, np.int8)
+    s = np.empty(1, np.float32)
+    nslow = shim.shim_quantize(x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), x.size,
+                               float(np.float32(amax16)), float(qmax),
+                               q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)),
+                               s.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return q, s[0], nslow
+
+
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_fast_path_matches_oracle_exhaustively(shim, oracle, qmax):
+    rng = np.random.default_rng(17)
+    # 160 scales spread over the whole fp16 range, plus the edges
+    amax_bits = np.unique(np.concatenate([
+        rng.integers(0x0001, 0x7BFF, size=160), [0x0001, 0x03FF, 0x0400, 0x3C00, 0x57F0, 0x7BFF]
+    ])).astype(np.uint16)
+    total_slow = 0
+    for ab in amax_bits.tolist():
+        pos = np.arange(0, ab + 1, dtype=np.uint16)
+        xs = np.concatenate([pos, pos | 0x8000]).view(np.float16)
+        row = np.concatenate([[np.uint16(ab).view(np.float16)], xs])[None, :]
+        want_q, want_s = oracle.quantize(row, 0, qmax)
+        got_q, got_s, nslow = _run(shim, row[0], row[0, 0], qmax)
+        total_slow += nslow
+        assert got_s == want_s[0]
+        np.testing.assert_array_equal(got_q, want_q[0], err_msg=f"amax bits {ab:#06x}")
+    # the guard is rare: well under 0.1 % of elements take the division rule
+    assert total_slow > 0
+
+
+def test_guard_is_needed(shim, oracle):
+    """Without the guard the reciprocal shortcut does disagree somewhere --
+    so the exhaustive test above is a real check of the guard."""
+    rng = np.random.default_rng(3)
+    mismatches = 0
+    for ab in rng.integers(0x0400, 0x7BFF, size=200).tolist():
+        pos = np.arange(0, ab + 1, dtype=np.uint16)
+        row = np.concatenate([[ab], pos]).astype(np.uint16).view(np.float16)[None, :]
+        want_q, _ = oracle.quantize(row, 0, 127)
+        x = row[0].astype(np.float32)
+        q = np.empty(x.shape, np.int8)
+        shim.shim_fast_only(x.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), x.size,
+                            float(x[0]), 127.0, q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)))
+        mismatches += int((q != want_q[0]).sum())
+        if mismatches:
+            break
+    assert mismatches > 0

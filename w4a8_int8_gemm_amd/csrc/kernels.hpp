@@ -1,0 +1,43 @@
+// Launchers of the library's kernels (host side).  Arguments are validated by
+// the C entry points before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace w4a8 {
+
+// Quantize `rows` fp16 rows of length K (K % 8 == 0) with slices of gs
+// (0 = whole row, 64, 128).  q is int8 [rows, K], or packed uint8
+// [rows, K/2] when int4; scale is fp32 [rows] or [rows, K/gs].
+void launch_quantize_rows(const uint16_t *x, int64_t rows, int K, int gs, float qmax, void *q,
+                          float *scale, bool int4, hipStream_t st);
+
+// What the GEMM's epilogue does with the int32 sums.
+enum class GemmMode : int {
+    PC = 0,          // fp16 y = c * sa[m] * sw[n]
+    I32 = 1,         // int32 c
+    PG = 2,          // fp16 y = sum_g P_g * sa[m,g] * sw[n,g]
+    PG_PARTIALS = 3, // int32 P [G, M, N]
+    W4 = 4,          // fp16 y = sa[m] * sum_g P_g * sw[n,g]   (int4 weights)
+    W4_PARTIALS = 5  // int32 P [G, M, N]                       (int4 weights)
+};
+
+struct GemmArgs {
+    const int8_t *xq;     // [M, K]
+    const float *sa;      // [M] or [M, G]
+    const void *w;        // int8 [N, K] or packed int4 [N, K/2]
+    const float *sw;      // [N] or [N, G]
+    void *out;            // fp16 [M, N] or int32 [M, N] / [G, M, N]
+    int M, N, K, gs;
+};
+
+void launch_gemm(GemmMode mode, const GemmArgs &a, hipStream_t st);
+
+// Decode matrix-vector: quantize the token, y[n] = rescale(sum_k q[k] w[n,k]).
+void launch_int8_mv(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, int N,
+                    int K, int8_t *xq_out, float *xs_out, hipStream_t st);
+
+}  // namespace w4a8

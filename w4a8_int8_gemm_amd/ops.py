@@ -1,0 +1,202 @@
+"""torch-tensor wrappers over the C entry points (marshalling only).
+
+Each function checks dtype, device and contiguity, allocates missing outputs
+with torch, and calls the library on torch's current stream of the tensors'
+device.  Outputs may be passed in (``out=...``) to avoid allocations.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import Mode, check, lib
+
+
+def _need(t, dtype, name, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _out(t, shape, dtype, like, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _need(t, dtype, name, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _st(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def is_available() -> bool:
+    """True if the current HIP device is a gfx950 GPU."""
+    return bool(lib().w4a8_is_available())
+
+
+def _scale_shape(rows, K, group_size):
+    return (rows,) if group_size == 0 else (rows, K // group_size if group_size > 0 else 0)
+
+
+def quantize_act(x, group_size: int = 0, out=None, scale=None):
+    """fp16 [M, K] -> (int8 [M, K], fp32 [M] or [M, K/gs])."""
+    _need(x, torch.float16, "x", 2)
+    M, K = x.shape
+    out = _out(out, (M, K), torch.int8, x, "out")
+    scale = _out(scale, _scale_shape(M, K, group_size), torch.float32, x, "scale")
+    with torch.cuda.device(x.device):
+        check(lib().quantize_act(_p(x), M, K, group_size, _p(out), _p(scale), _st(x)))
+    return out, scale
+
+
+def quantize_weight_int8(w, group_size: int = 0, out=None, scale=None):
+    """fp16 [N, K] -> (int8 [N, K], fp32 [N] or [N, K/gs])."""
+    _need(w, torch.float16, "w", 2)
+    N, K = w.shape
+    out = _out(out, (N, K), torch.int8, w, "out")
+    scale = _out(scale, _scale_shape(N, K, group_size), torch.float32, w, "scale")
+    with torch.cuda.device(w.device):
+        check(lib().quantize_weight_int8(_p(w), N, K, group_size, _p(out), _p(scale), _st(w)))
+    return out, scale
+
+
+def pack_weight_int4(w, group_size: int = 128, out=None, scale=None):
+    """fp16 [N, K] -> (packed uint8 [N, K/2], fp32 [N, K/gs])."""
+    _need(w, torch.float16, "w", 2)
+    N, K = w.shape
+    out = _out(out, (N, K // 2), torch.uint8, w, "out")
+    scale = _out(scale, (N, K // group_size if group_size > 0 else 0), torch.float32, w, "scale")
+    with torch.cuda.device(w.device):
+        check(lib().pack_weight_int4(_p(w), N, K, group_size, _p(out), _p(scale), _st(w)))
+    return out, scale
+
+
+def _gemm_shapes(xq, w, packed):
+    _need(xq, torch.int8, "xq", 2)
+    _need(w, torch.uint8 if packed else torch.int8, "w", 2)
+    M, K = xq.shape
+    N = w.shape[0]
+    if w.shape[1] * (2 if packed else 1) != K:
+        raise ValueError(f"weight shape {tuple(w.shape)} does not match K={K}")
+    return M, N, K
+
+
+def w8a8_gemm_pc(xq, x_scale, wq, w_scale, out=None):
+    """y fp16 [M, N] = (xq . wq^T) * x_scale[m] * w_scale[n]."""
+    M, N, K = _gemm_shapes(xq, wq, False)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    out = _out(out, (M, N), torch.float16, xq, "out")
+    with torch.cuda.device(xq.device):
+        check(lib().w8a8_gemm_pc(_p(xq), _p(x_scale), _p(wq), _p(w_scale), _p(out), M, N, K,
+                                 _st(xq)))
+    return out
+
+
+def w8a8_gemm_pg(xq, x_scale, wq, w_scale, group_size: int, out=None):
+    """Per-group W8A8: x_scale [M, K/gs], w_scale [N, K/gs]."""
+    M, N, K = _gemm_shapes(xq, wq, False)
+    _need(x_scale, torch.float32, "x_scale", 2)
+    _need(w_scale, torch.float32, "w_scale", 2)
+    out = _out(out, (M, N), torch.float16, xq, "out")
+    with torch.cuda.device(xq.device):
+        check(lib().w8a8_gemm_pg(_p(xq), _p(x_scale), _p(wq), _p(w_scale), group_size, _p(out),
+                                 M, N, K, _st(xq)))
+    return out
+
+
+def w4a8_gemm(xq, x_scale, w4, w_scale, group_size: int, out=None):
+    """W4A8: per-token x_scale [M], packed w4 [N, K/2], w_scale [N, K/gs]."""
+    M, N, K = _gemm_shapes(xq, w4, True)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    _need(w_scale, torch.float32, "w_scale", 2)
+    out = _out(out, (M, N), torch.float16, xq, "out")
+    with torch.cuda.device(xq.device):
+        check(lib().w4a8_gemm(_p(xq), _p(x_scale), _p(w4), _p(w_scale), group_size, _p(out),
+                              M, N, K, _st(xq)))
+    return out
+
+
+def int8_mv(x, wq, w_scale, out=None, return_codes: bool = False):
+    """Decode: x fp16 [K] (or [1, K]) -> y fp16 [N]; optionally also (codes, scale)."""
+    if x.dim() == 2 and x.shape[0] == 1:
+        x = x.reshape(-1)
+    _need(x, torch.float16, "x", 1)
+    _need(wq, torch.int8, "wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    K = x.shape[0]
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("wq does not match K")
+    out = _out(out, (N,), torch.float16, x, "out")
+    xq = torch.empty((K,), dtype=torch.int8, device=x.device) if return_codes else None
+    xs = torch.empty((1,), dtype=torch.float32, device=x.device) if return_codes else None
+    with torch.cuda.device(x.device):
+        check(lib().int8_mv(_p(x), _p(wq), _p(w_scale), _p(out), N, K, _p(xq), _p(xs), _st(x)))
+    return (out, xq, xs) if return_codes else out
+
+
+def linear_workspace_size(mode, M: int, K: int, group_size: int = 0) -> int:
+    return int(lib().linear_workspace_size(int(mode), M, K, group_size))
+
+
+def linear(mode, x, w, w_scale, group_size: int = 0, workspace=None, out=None):
+    """The whole layer: int8_mv when M == 1 in per-channel mode, else quantize + GEMM."""
+    mode = Mode(mode)
+    _need(x, torch.float16, "x", 2)
+    packed = mode == Mode.W4A8
+    _need(w, torch.uint8 if packed else torch.int8, "w", 2)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] * (2 if packed else 1) != K:
+        raise ValueError("weight shape does not match K")
+    need = linear_workspace_size(mode, M, K, group_size)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    out = _out(out, (M, N), torch.float16, x, "out")
+    with torch.cuda.device(x.device):
+        check(lib().linear(int(mode), _p(x), M, K, _p(w), _p(w_scale), group_size, N, _p(out),
+                           _p(workspace), workspace.numel(), _st(x)))
+    return out
+
+
+def w8a8_gemm_i32(xq, wq, out=None):
+    """Raw int32 sums [M, N] of the per-channel GEMM's main loop."""
+    M, N, K = _gemm_shapes(xq, wq, False)
+    out = _out(out, (M, N), torch.int32, xq, "out")
+    with torch.cuda.device(xq.device):
+        check(lib().w8a8_gemm_i32(_p(xq), _p(wq), _p(out), M, N, K, _st(xq)))
+    return out
+
+
+def w8a8_gemm_pg_partials(xq, wq, group_size: int, out=None):
+    """Per-group int32 partial sums [K/gs, M, N]."""
+    M, N, K = _gemm_shapes(xq, wq, False)
+    out = _out(out, (K // group_size, M, N), torch.int32, xq, "out")
+    with torch.cuda.device(xq.device):
+        check(lib().w8a8_gemm_pg_partials(_p(xq), _p(wq), group_size, _p(out), M, N, K, _st(xq)))
+    return out
+
+
+def w4a8_gemm_partials(xq, w4, group_size: int, out=None):
+    """Per-group int32 partial sums [K/gs, M, N] against unpacked int4 codes."""
+    M, N, K = _gemm_shapes(xq, w4, True)
+    out = _out(out, (K // group_size, M, N), torch.int32, xq, "out")
+    with torch.cuda.device(xq.device):
+        check(lib().w4a8_gemm_partials(_p(xq), _p(w4), group_size, _p(out), M, N, K, _st(xq)))
+    return out
