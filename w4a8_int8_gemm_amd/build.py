@@ -2,7 +2,8 @@
 
 Each translation unit is compiled by hipcc in parallel, then linked into one
 shared library next to this file.  Packed-fp32 instructions are disabled for
-all device code.
+all device code, and floating-point contraction is off: every fp32 operation
+rounds as written (explicit fmaf where a fused multiply-add is meant).
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "mv.hip"]
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]

@@ -21,10 +21,17 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// fp16 bits <-> fp32.  Widening is exact; narrowing rounds to nearest even
-// (v_cvt_f16_f32 under the default rounding mode).
+// fp16 bits <-> fp32.  Widening is exact; narrowing rounds the fp32 value to
+// nearest even (v_cvt_f16_f32).  The empty asm keeps the instruction selector
+// from fusing a preceding fp32 multiply into the conversion (v_fma_mixlo_f16
+// rounds once, straight to fp16), so every kernel rounds the same fp32 value
+// the same way.
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
-__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ uint16_t f2h(float f)
+{
+    asm("" : "+v"(f));
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
 
 // Two fp16 values (low, high half of a dword) to fp32.
 __device__ __forceinline__ float lo_h2f(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }

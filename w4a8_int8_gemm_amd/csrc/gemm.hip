@@ -29,6 +29,8 @@
 //    through LDS together with the tiles.
 //  * Workgroups are remapped so that each XCD (one L2 each) works on a
 //    contiguous range of tiles, ordered in groups of `group_m` tile rows.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace w4a8 {
@@ -62,6 +64,15 @@ template <GemmMode MODE> struct ModeTraits {
     static constexpr bool fold_sw = (MODE == GemmMode::PG || MODE == GemmMode::W4);
 };
 
+// Workgroup barrier that orders LDS accesses only: global loads stay in
+// flight across it (a full __syncthreads would also wait for them).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int BM, int BN, int WM, int WN, GemmMode MODE, int GS>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int tiles_m,
                                                            int tiles_n, int group_m)
@@ -72,7 +83,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     constexpr int FM = TM / 16, FN = TN / 16;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
     constexpr int XCH = BM * 8;                       // 16-byte chunks of X per stage
-    constexpr int WCH = T::int4 ? BN * 4 : BN * 8;    // 16-byte chunks of W per stage (as loaded)
+    constexpr int CPR = T::int4 ? 4 : 8;              // loaded 16-byte chunks per W row per stage
+    constexpr int WCH = BN * CPR;
     constexpr int XIT = (XCH + NT - 1) / NT;
     constexpr int WIT = (WCH + NT - 1) / NT;
     // groups per stage (gs 64: two, gs 128: one); scales staged per group
@@ -113,41 +125,64 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     const uint8_t *__restrict__ wb = static_cast<const uint8_t *>(args.w);
     const int wrow = T::int4 ? K / 2 : K;             // bytes per weight row
 
-    // ---- staging registers
-    uint4 xr[XIT];
-    uint4 wr[WIT];
-    float sar[T::fold_sa ? 1 : 1][NG];
-    float swr[NG];
+    // Per-thread global source offsets of its chunks (row clamped to the
+    // matrix, so edge tiles read valid memory; those rows are never stored).
+    int64_t xoff[XIT], woff[WIT];
+#pragma unroll
+    for (int it = 0; it < XIT; ++it) {
+        const int q = min(tid + it * NT, XCH - 1);
+        xoff[it] = (int64_t)min(m0 + (q >> 3), M - 1) * K + (q & 7) * 16;
+    }
+#pragma unroll
+    for (int it = 0; it < WIT; ++it) {
+        const int q = min(tid + it * NT, WCH - 1);
+        woff[it] = (int64_t)min(n0 + q / CPR, N - 1) * wrow + (q % CPR) * 16;
+    }
 
-    auto load_stage = [&](int s) {
+    // ---- register staging: two stages in flight
+    struct Stage {
+        uint4 x[XIT];
+        uint4 w[WIT];
+        float sa[NG];
+        float sw[NG];
+    };
+    Stage st0;
+    [[maybe_unused]] Stage st1;
+
+    auto load_stage = [&](Stage &S, int s) {
         const int k0 = s * BK;
-#pragma unroll
-        for (int it = 0; it < XIT; ++it) {
-            const int q = tid + it * NT;
-            const int row = q >> 3, c = q & 7;
-            const int gr = min(m0 + row, M - 1);
-            const bool ok = (q < XCH) && (k0 + c * 16 < K);
-            xr[it] = ok ? *reinterpret_cast<const uint4 *>(xq + (int64_t)gr * K + k0 + c * 16)
-                        : make_uint4(0u, 0u, 0u, 0u);
-        }
-        constexpr int cpr = T::int4 ? 4 : 8;          // loaded chunks per row per stage
         const int kb0 = T::int4 ? k0 / 2 : k0;
+        if (k0 + BK <= K) {
 #pragma unroll
-        for (int it = 0; it < WIT; ++it) {
-            const int q = tid + it * NT;
-            const int row = q / cpr, c = q % cpr;
-            const int gr = min(n0 + row, N - 1);
-            const bool ok = (q < WCH) && (kb0 + c * 16 < wrow);
-            wr[it] = ok ? *reinterpret_cast<const uint4 *>(wb + (int64_t)gr * wrow + kb0 + c * 16)
-                        : make_uint4(0u, 0u, 0u, 0u);
+            for (int it = 0; it < XIT; ++it)
+                S.x[it] = *reinterpret_cast<const uint4 *>(xq + xoff[it] + k0);
+#pragma unroll
+            for (int it = 0; it < WIT; ++it)
+                S.w[it] = *reinterpret_cast<const uint4 *>(wb + woff[it] + kb0);
+        } else {
+            // last stage of a K with K % 128 == 64: the upper half is zero
+#pragma unroll
+            for (int it = 0; it < XIT; ++it) {
+                const int c = (tid + it * NT) & 7;
+                const bool ok = k0 + c * 16 < K;
+                const uint4 v = *reinterpret_cast<const uint4 *>(xq + xoff[it] + (ok ? k0 : K - 16 - c * 16));
+                S.x[it] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int it = 0; it < WIT; ++it) {
+                const int c = (tid + it * NT) % CPR;
+                const bool ok = kb0 + c * 16 < wrow;
+                const uint4 v = *reinterpret_cast<const uint4 *>(wb + woff[it] + (ok ? kb0 : wrow - 16 - c * 16));
+                S.w[it] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
         if constexpr (T::fold_sa) {
             if (tid < BM) {
                 const int gr = min(m0 + tid, M - 1);
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
-                    const int gi = s * NG + g;
-                    sar[0][g] = (gi < G) ? args.sa[(int64_t)gr * G + gi] : 0.0f;
+                    const int gi = min(s * NG + g, G - 1);
+                    S.sa[g] = args.sa[(int64_t)gr * G + gi];
                 }
             }
         }
@@ -156,40 +191,40 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                 const int gr = min(n0 + tid, N - 1);
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
-                    const int gi = s * NG + g;
-                    float v = (gi < G) ? args.sw[(int64_t)gr * G + gi] : 0.0f;
+                    const int gi = min(s * NG + g, G - 1);
+                    float v = args.sw[(int64_t)gr * G + gi];
                     if constexpr (T::int4)
                         v *= 0.0625f;                 // undo the x16 of the unpacked codes (exact)
-                    swr[g] = v;
+                    S.sw[g] = v;
                 }
             }
         }
     };
 
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](const Stage &S, int buf) {
 #pragma unroll
         for (int it = 0; it < XIT; ++it) {
             const int q = tid + it * NT;
-            if (q < XCH) {
+            if (XCH % NT == 0 || q < XCH) {
                 const int row = q >> 3, c = q & 7;
-                *reinterpret_cast<uint4 *>(&xs[buf][row * BK + swz(row, c) * 16]) = xr[it];
+                *reinterpret_cast<uint4 *>(&xs[buf][row * BK + swz(row, c) * 16]) = S.x[it];
             }
         }
 #pragma unroll
         for (int it = 0; it < WIT; ++it) {
             const int q = tid + it * NT;
-            if (q < WCH) {
+            if (WCH % NT == 0 || q < WCH) {
                 if constexpr (T::int4) {
                     const int row = q >> 2, c = q & 3;    // packed chunk c -> int8 chunks 2c, 2c+1
-                    const uint2 a = unpack_int4x8(wr[it].x), b = unpack_int4x8(wr[it].y);
-                    const uint2 d = unpack_int4x8(wr[it].z), e = unpack_int4x8(wr[it].w);
+                    const uint2 a = unpack_int4x8(S.w[it].x), b = unpack_int4x8(S.w[it].y);
+                    const uint2 d = unpack_int4x8(S.w[it].z), e = unpack_int4x8(S.w[it].w);
                     *reinterpret_cast<uint4 *>(&ws[buf][row * BK + swz(row, 2 * c) * 16]) =
                         make_uint4(a.x, a.y, b.x, b.y);
                     *reinterpret_cast<uint4 *>(&ws[buf][row * BK + swz(row, 2 * c + 1) * 16]) =
                         make_uint4(d.x, d.y, e.x, e.y);
                 } else {
                     const int row = q >> 3, c = q & 7;
-                    *reinterpret_cast<uint4 *>(&ws[buf][row * BK + swz(row, c) * 16]) = wr[it];
+                    *reinterpret_cast<uint4 *>(&ws[buf][row * BK + swz(row, c) * 16]) = S.w[it];
                 }
             }
         }
@@ -197,14 +232,14 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
             if (tid < BM) {
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
-                    sas[buf][g * BM + tid] = sar[0][g];
+                    sas[buf][g * BM + tid] = S.sa[g];
             }
         }
         if constexpr (T::fold_sw) {
             if (tid < BN) {
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
-                    sws[buf][g * BN + tid] = swr[g];
+                    sws[buf][g * BN + tid] = S.sw[g];
             }
         }
     };
@@ -234,6 +269,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     // output coordinates of this lane inside a 16x16 block
     const int out_m = lane & 15;
     const int out_n = (lane >> 4) * 4;
+    // swizzled byte offsets of the lane's fragment chunk for kk = 0, 1 (the
+    // swizzle depends on the row only through lane%16, since bases are multiples of 16)
+    const int xo0 = xrow0 * BK + swz(lrow, lchunk) * 16;
+    const int xo1 = xrow0 * BK + swz(lrow, 4 + lchunk) * 16;
+    const int wo0 = wrow0 * BK + swz(lrow, lchunk) * 16;
+    const int wo1 = wrow0 * BK + swz(lrow, 4 + lchunk) * 16;
 
     auto store_partials = [&](int g) {
         int32_t *P = static_cast<int32_t *>(args.out) + (int64_t)g * M * N;
@@ -281,58 +322,84 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                 }
     };
 
-    // ---- prologue
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-
-    // ---- main loop
-    for (int s = 0; s < nstage; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nstage)
-            load_stage(s + 1);
+    // One 64-wide k step from LDS buffer `buf`.
+    auto mma_step = [&](int buf, int kk, bool restart) {
         const int8_t *xb = xs[buf];
         const int8_t *wbuf = ws[buf];
+        const int xo = kk ? xo1 : xo0, wo = kk ? wo1 : wo0;
+        v4i bf[FM], af[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            bf[i] = *reinterpret_cast<const v4i *>(xb + xo + i * 16 * BK);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            af[j] = *reinterpret_cast<const v4i *>(wbuf + wo + j * 16 * BK);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[j], bf[i],
+                                                                  restart ? zero : acc[j][i], 0, 0, 0);
+    };
+
+    auto compute_stage = [&](int buf, int s) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int kc = s * 2 + kk;
             if (kc < nkc) {
-                const int chunk = kk * 4 + lchunk;
-                v4i bf[FM], af[FN];
-#pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    const int r = xrow0 + i * 16;
-                    bf[i] = *reinterpret_cast<const v4i *>(xb + r * BK + swz(r, chunk) * 16);
-                }
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int r = wrow0 + j * 16;
-                    af[j] = *reinterpret_cast<const v4i *>(wbuf + r * BK + swz(r, chunk) * 16);
-                }
                 // per-group modes start every group from zero
-                const bool restart = T::pergroup && (GS == 64 || kk == 0);
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-                        acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                            af[j], bf[i], restart ? zero : acc[j][i], 0, 0, 0);
+                mma_step(buf, kk, T::pergroup && (GS == 64 || kk == 0));
                 if constexpr (T::pergroup) {
-                    const bool group_end = (GS == 64) || (kk == 1) || (kc + 1 == nkc);
-                    if (group_end) {
+                    if (GS == 64 || kk == 1 || kc + 1 == nkc) {
                         const int g = (GS == 64) ? kc : s;
-                        const int gl = (GS == 64) ? kk : 0;     // slot of the group in this stage
                         if constexpr (T::partials)
                             store_partials(g);
                         else
-                            fold_group(buf, gl);
+                            fold_group(buf, (GS == 64) ? kk : 0);
                     }
                 }
             }
         }
-        if (s + 1 < nstage)
-            store_stage(buf ^ 1);
-        __syncthreads();
+    };
+
+    // ---- pipeline.  Stage s is computed from LDS buffer s&1.  Without fp32
+    // accumulators (per-channel) two register sets keep the loads of stages
+    // s+1 and s+2 in flight; the per-group modes, which hold fp32
+    // accumulators too, keep one stage in flight to stay within registers.
+    if constexpr (!T::pergroup) {
+        load_stage(st0, 0);
+        if (nstage > 1)
+            load_stage(st1, 1);
+        store_stage(st0, 0);
+        lds_barrier();
+        auto iteration = [&](auto P, int s) {
+            constexpr int p = decltype(P)::value;
+            Stage &cur = p == 0 ? st0 : st1;    // held stage s (already in LDS)
+            Stage &nxt = p == 0 ? st1 : st0;    // holds stage s+1
+            if (s + 2 < nstage)
+                load_stage(cur, s + 2);
+            compute_stage(p, s);
+            if (s + 1 < nstage)
+                store_stage(nxt, p ^ 1);
+            lds_barrier();
+        };
+        for (int s = 0; s < nstage; s += 2) {
+            iteration(std::integral_constant<int, 0>(), s);
+            if (s + 1 < nstage)
+                iteration(std::integral_constant<int, 1>(), s + 1);
+        }
+    } else {
+        load_stage(st0, 0);
+        store_stage(st0, 0);
+        lds_barrier();
+        for (int s = 0; s < nstage; ++s) {
+            if (s + 1 < nstage)
+                load_stage(st0, s + 1);
+            compute_stage(s & 1, s);
+            if (s + 1 < nstage)
+                store_stage(st0, (s + 1) & 1);
+            lds_barrier();
+        }
     }
 
     // ---- epilogue
@@ -371,6 +438,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                     swv[j][r] = args.sw[min(n + r, N - 1)];
             }
         }
+        const bool vec_ok = (N & 3) == 0;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = m0 + wm * TM + i * 16 + out_m;
@@ -391,7 +459,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                         v[r] = accf[j][i][r] * sa;     // W4: per-token scale last
                 }
                 uint16_t *dst = Y + (int64_t)m * N + n;
-                if (n + 3 < N && (N & 3) == 0) {
+                if (vec_ok && n + 3 < N) {
                     *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_h2(v[0], v[1]),
                                                                  pack_h2(v[2], v[3]));
                 } else {
