@@ -8,18 +8,21 @@
 // "입도: Per-Tensor vs. Per-Channel vs. Per-Group").  INT4 weights are
 // unpacked to INT8 before the INT8 matmul ("cider" post, modes table).
 //
-// Design (CDNA4, wave64):
+// Design (CDNA4, wave64, one wave per SIMD for the large tiles):
 //  * One workgroup computes a BM x BN tile of Y (m x n) with WM x WN waves.
-//    Both operands are K-contiguous, the natural layout for MFMA: the weight
-//    tile feeds the MFMA's A operand (16 n-rows x 64 k per
-//    v_mfma_i32_16x16x64_i8) and the activation tile its B operand, so each
-//    lane's four int32 results are four consecutive n of one output row and
-//    the epilogue stores 8 contiguous bytes per lane.
-//  * K advances in stages of 128 bytes.  Global loads for stage s+1 are
-//    issued into registers before the MFMAs of stage s, then written to the
-//    other half of a double-buffered LDS tile.  16-byte chunks are XOR-
-//    swizzled per row so that the ds_read_b128 fragment loads hit distinct
-//    banks with either 32 or 64 four-byte banks.
+//    Both operands are K-contiguous.  v_mfma_i32_32x32x32_i8 takes the
+//    weight fragment as its A operand (32 n-rows x 32 k, 16 bytes per lane)
+//    and the activation fragment as B, so each lane's int32 results come in
+//    runs of four consecutive n of one output row (8-byte fp16 stores).  This
+//    MFMA sustains close to the int8 peak with a single wave per SIMD, which
+//    the large per-wave tiles need (they keep LDS traffic per op low).
+//  * K advances in stages of 128 bytes through three LDS buffers.  Global
+//    loads for stages s+2 and s+3 are in flight in two register sets while
+//    stage s is computed; stage s+2 is written to LDS at the end of stage s,
+//    so stage s+1 is already resident when stage s ends and its first
+//    fragments are read while the last MFMAs of stage s run.  Within a stage
+//    the fragments of k-step t+1 are read while the MFMAs of step t run.
+//  * 16-byte chunks are XOR-swizzled per LDS row.
 //  * int4 weights are loaded packed (half the bytes), unpacked in registers to
 //    16 * code (the nibble placed in the high half of each byte, which is
 //    the code times 16 as a signed byte) and stored to LDS in the same int8
@@ -37,10 +40,13 @@ namespace w4a8 {
 
 namespace {
 
-constexpr int BK = 128;          // k bytes per LDS stage (two 64-wide MFMA steps)
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 128;          // k bytes per LDS stage (four 32-wide MFMA steps)
 
 // Physical 16-byte chunk of logical chunk c (0..7) in LDS row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
 
 // Unpack 8 int4 codes (one dword, low nibble = even k) into 8 signed bytes
 // holding 16 * code, in natural k order (two dwords).
@@ -54,6 +60,15 @@ __device__ __forceinline__ uint2 unpack_int4x8(uint32_t x)
     return make_uint2(a, b);
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads stay in
+// flight across it (a full __syncthreads would also wait for them).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <GemmMode MODE> struct ModeTraits {
     static constexpr bool int4 = (MODE == GemmMode::W4 || MODE == GemmMode::W4_PARTIALS);
     static constexpr bool pergroup = (MODE == GemmMode::PG || MODE == GemmMode::PG_PARTIALS ||
@@ -64,13 +79,43 @@ template <GemmMode MODE> struct ModeTraits {
     static constexpr bool fold_sw = (MODE == GemmMode::PG || MODE == GemmMode::W4);
 };
 
-// Workgroup barrier that orders LDS accesses only: global loads stay in
-// flight across it (a full __syncthreads would also wait for them).
-__device__ __forceinline__ void lds_barrier()
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS copies: each lane's bytes from global memory land at
+// M0 + size * lane.  Issued through asm so that the only waits on them are
+// the kernel's own (vmcnt before the barrier that publishes a stage); the
+// "memory" clobber keeps other memory accesses from moving across them.  M0
+// is saved and restored around the copy, and one wait state separates the
+// SALU write of M0 from the load that reads it (a gfx9 hazard).
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    return (uint32_t)(uintptr_t)(const lds_void *)p;
+}
+__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(lds), "v"(src)
+                 : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(lds), "v"(src)
+                 : "memory");
+}
+
+// s_waitcnt that waits for the vector-memory counter only (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maximum).
+template <int N> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 template <int BM, int BN, int WM, int WN, GemmMode MODE, int GS>
@@ -78,27 +123,60 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                                                            int tiles_n, int group_m)
 {
     using T = ModeTraits<MODE>;
-    constexpr int NT = WM * WN * 64;
+    constexpr int NW = WM * WN;                       // waves
     constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 16, FN = TN / 16;
-    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
-    constexpr int XCH = BM * 8;                       // 16-byte chunks of X per stage
-    constexpr int CPR = T::int4 ? 4 : 8;              // loaded 16-byte chunks per W row per stage
-    constexpr int WCH = BN * CPR;
-    constexpr int XIT = (XCH + NT - 1) / NT;
-    constexpr int WIT = (WCH + NT - 1) / NT;
-    // groups per stage (gs 64: two, gs 128: one); scales staged per group
-    constexpr int NG = (GS == 64) ? 2 : 1;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+    constexpr int XBUF = BM * BK, WBUF = BN * BK;
+    // direct-to-LDS copies: one wave instruction moves 1 KiB = 8 rows of a stage
+    constexpr int XB = XBUF / 1024 / NW;              // X blocks per wave per stage
+    static_assert(XBUF % (1024 * NW) == 0, "X stage must split evenly over the waves");
+    constexpr bool kDmaW = !T::int4;                  // int8 weights go straight to LDS
+    constexpr int WB = kDmaW ? WBUF / 1024 / NW : 0;
+    static_assert(!kDmaW || WBUF % (1024 * NW) == 0, "W stage must split evenly over the waves");
+    // packed int4 weights are staged through registers and unpacked
+    constexpr int WCH4 = BN * 4;                      // 16-byte packed chunks per stage
+    constexpr int WIT4 = T::int4 ? (WCH4 + NW * 64 - 1) / (NW * 64) : 0;
+    constexpr int NG = T::pergroup ? BK / GS : 1;     // groups per stage
+    constexpr int SPG = T::pergroup ? GS / 32 : 4;    // k-steps per group
+    // scale copies (4 bytes per lane): per stage NG*BM activation scales and
+    // NG*BN weight scales, in instructions of 64 lanes, dealt round-robin
+    constexpr int SA_I = T::fold_sa ? (NG * BM + 63) / 64 : 0;
+    constexpr int SW_I = T::fold_sw ? (NG * BN + 63) / 64 : 0;
+    // copies every wave issues per stage (a lower bound where the scale
+    // instructions do not split evenly; waiting on it is conservative)
+    constexpr int ND = XB + WB + SA_I / NW + SW_I / NW;
 
-    __shared__ __attribute__((aligned(16))) int8_t xs[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) int8_t ws[2][BN * BK];
-    __shared__ __attribute__((aligned(16))) float sas[2][T::fold_sa ? NG * BM : 1];
-    __shared__ __attribute__((aligned(16))) float sws[2][T::fold_sw ? NG * BN : 1];
+    __shared__ __attribute__((aligned(1024))) int8_t xs0[XBUF];
+    __shared__ __attribute__((aligned(1024))) int8_t xs1[XBUF];
+    __shared__ __attribute__((aligned(1024))) int8_t xs2[XBUF];
+    __shared__ __attribute__((aligned(1024))) int8_t ws0[WBUF];
+    __shared__ __attribute__((aligned(1024))) int8_t ws1[WBUF];
+    __shared__ __attribute__((aligned(1024))) int8_t ws2[WBUF];
+    constexpr int SAL = T::fold_sa ? NG * BM : 1, SWL = T::fold_sw ? NG * BN : 1;
+    __shared__ __attribute__((aligned(16))) float sa0[SAL], sa1[SAL], sa2[SAL];
+    __shared__ __attribute__((aligned(16))) float sw0[SWL], sw1[SWL], sw2[SWL];
+    auto XS = [&](auto B) __attribute__((always_inline)) -> int8_t * {
+        constexpr int b = decltype(B)::value;
+        return b == 0 ? xs0 : (b == 1 ? xs1 : xs2);
+    };
+    auto WS = [&](auto B) __attribute__((always_inline)) -> int8_t * {
+        constexpr int b = decltype(B)::value;
+        return b == 0 ? ws0 : (b == 1 ? ws1 : ws2);
+    };
+    auto SAS = [&](auto B) __attribute__((always_inline)) -> float * {
+        constexpr int b = decltype(B)::value;
+        return b == 0 ? sa0 : (b == 1 ? sa1 : sa2);
+    };
+    auto SWS = [&](auto B) __attribute__((always_inline)) -> float * {
+        constexpr int b = decltype(B)::value;
+        return b == 0 ? sw0 : (b == 1 ? sw1 : sw2);
+    };
 
     const int M = args.M, N = args.N, K = args.K;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
     // ---- tile selection: XCD-contiguous ranges, grouped along m
@@ -119,288 +197,311 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     const int m0 = tm * BM, n0 = tn * BN;
     const int G = T::pergroup ? K / GS : 1;
     const int nstage = (K + BK - 1) / BK;
-    const int nkc = K / 64;                           // 64-wide MFMA steps in K
+    const int nks = K / 32;                           // 32-wide MFMA steps in K
 
     const int8_t *__restrict__ xq = args.xq;
     const uint8_t *__restrict__ wb = static_cast<const uint8_t *>(args.w);
     const int wrow = T::int4 ? K / 2 : K;             // bytes per weight row
 
-    // Per-thread global source offsets of its chunks (row clamped to the
-    // matrix, so edge tiles read valid memory; those rows are never stored).
-    int64_t xoff[XIT], woff[WIT];
+    // Direct-to-LDS source offsets.  A wave instruction writes lane l's 16
+    // bytes at LDS block + 16*l, i.e. row 8*blk + l/8, physical chunk l%8; the
+    // lane therefore fetches the logical chunk that the swizzle puts there.
+    const int dma_row = lane >> 3;
+    const int dma_chunk = (lane & 7) ^ (dma_row & 7);
+    int64_t xoff[XB];
 #pragma unroll
-    for (int it = 0; it < XIT; ++it) {
-        const int q = min(tid + it * NT, XCH - 1);
-        xoff[it] = (int64_t)min(m0 + (q >> 3), M - 1) * K + (q & 7) * 16;
+    for (int i = 0; i < XB; ++i) {
+        const int row = (wave + NW * i) * 8 + dma_row;
+        xoff[i] = (int64_t)min(m0 + row, M - 1) * K + dma_chunk * 16;
     }
+    int64_t woff[WB > 0 ? WB : 1];
 #pragma unroll
-    for (int it = 0; it < WIT; ++it) {
-        const int q = min(tid + it * NT, WCH - 1);
-        woff[it] = (int64_t)min(n0 + q / CPR, N - 1) * wrow + (q % CPR) * 16;
+    for (int i = 0; i < WB; ++i) {
+        const int row = (wave + NW * i) * 8 + dma_row;
+        woff[i] = (int64_t)min(n0 + row, N - 1) * K + dma_chunk * 16;
+    }
+    // packed int4 weights: thread -> (row, 16-byte packed chunk)
+    int64_t w4off[WIT4 > 0 ? WIT4 : 1];
+#pragma unroll
+    for (int it = 0; it < WIT4; ++it) {
+        const int q = min(tid + it * NW * 64, WCH4 - 1);
+        w4off[it] = (int64_t)min(n0 + (q >> 2), N - 1) * wrow + (q & 3) * 16;
     }
 
-    // ---- register staging: two stages in flight
-    struct Stage {
-        uint4 x[XIT];
-        uint4 w[WIT];
-        float sa[NG];
-        float sw[NG];
-    };
-    Stage st0;
-    [[maybe_unused]] Stage st1;
-
-    auto load_stage = [&](Stage &S, int s) {
+    // Issue the copies of stage s into LDS buffer B.
+    auto dma_stage = [&](auto B, int s) __attribute__((always_inline)) {
         const int k0 = s * BK;
-        const int kb0 = T::int4 ? k0 / 2 : k0;
-        if (k0 + BK <= K) {
+        const bool full = k0 + BK <= K;               // else: K % 128 == 64, upper half unused
+        const int kx = (full || k0 + dma_chunk * 16 < K) ? k0 : K - 16 - dma_chunk * 16;
 #pragma unroll
-            for (int it = 0; it < XIT; ++it)
-                S.x[it] = *reinterpret_cast<const uint4 *>(xq + xoff[it] + k0);
+        for (int i = 0; i < XB; ++i)
+            copy16_to_lds(xq + xoff[i] + kx, lds_addr(XS(B) + (wave + NW * i) * 1024));
 #pragma unroll
-            for (int it = 0; it < WIT; ++it)
-                S.w[it] = *reinterpret_cast<const uint4 *>(wb + woff[it] + kb0);
-        } else {
-            // last stage of a K with K % 128 == 64: the upper half is zero
-#pragma unroll
-            for (int it = 0; it < XIT; ++it) {
-                const int c = (tid + it * NT) & 7;
-                const bool ok = k0 + c * 16 < K;
-                const uint4 v = *reinterpret_cast<const uint4 *>(xq + xoff[it] + (ok ? k0 : K - 16 - c * 16));
-                S.x[it] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-            }
-#pragma unroll
-            for (int it = 0; it < WIT; ++it) {
-                const int c = (tid + it * NT) % CPR;
-                const bool ok = kb0 + c * 16 < wrow;
-                const uint4 v = *reinterpret_cast<const uint4 *>(wb + woff[it] + (ok ? kb0 : wrow - 16 - c * 16));
-                S.w[it] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
+        for (int i = 0; i < WB; ++i)
+            copy16_to_lds(wb + woff[i] + kx, lds_addr(WS(B) + (wave + NW * i) * 1024));
         if constexpr (T::fold_sa) {
-            if (tid < BM) {
-                const int gr = min(m0 + tid, M - 1);
 #pragma unroll
-                for (int g = 0; g < NG; ++g) {
+            for (int i = 0; i < (SA_I + NW - 1) / NW; ++i) {
+                const int ins = wave + NW * i;
+                if (SA_I % NW == 0 || ins < SA_I) {
+                    const int e = ins * 64 + lane;    // entry g*BM + r
+                    const int g = min(e / BM, NG - 1), r = e % BM;
                     const int gi = min(s * NG + g, G - 1);
-                    S.sa[g] = args.sa[(int64_t)gr * G + gi];
+                    if (e < NG * BM)
+                        copy4_to_lds(args.sa + (int64_t)min(m0 + r, M - 1) * G + gi,
+                                     lds_addr(SAS(B) + ins * 64));
                 }
             }
         }
         if constexpr (T::fold_sw) {
-            if (tid < BN) {
-                const int gr = min(n0 + tid, N - 1);
 #pragma unroll
-                for (int g = 0; g < NG; ++g) {
+            for (int i = 0; i < (SW_I + NW - 1) / NW; ++i) {
+                const int ins = wave + NW * i;
+                if (SW_I % NW == 0 || ins < SW_I) {
+                    const int e = ins * 64 + lane;    // entry g*BN + r
+                    const int g = min(e / BN, NG - 1), r = e % BN;
                     const int gi = min(s * NG + g, G - 1);
-                    float v = args.sw[(int64_t)gr * G + gi];
-                    if constexpr (T::int4)
-                        v *= 0.0625f;                 // undo the x16 of the unpacked codes (exact)
-                    S.sw[g] = v;
+                    if (e < NG * BN)
+                        copy4_to_lds(args.sw + (int64_t)min(n0 + r, N - 1) * G + gi,
+                                     lds_addr(SWS(B) + ins * 64));
                 }
             }
         }
     };
 
-    auto store_stage = [&](const Stage &S, int buf) {
+    // ---- packed int4 weights: register staging and unpack into LDS
+    uint4 w4r[WIT4 > 0 ? WIT4 : 1];
+    auto w4_load = [&](int s) __attribute__((always_inline)) {
+        const int kb0 = s * (BK / 2);
 #pragma unroll
-        for (int it = 0; it < XIT; ++it) {
-            const int q = tid + it * NT;
-            if (XCH % NT == 0 || q < XCH) {
-                const int row = q >> 3, c = q & 7;
-                *reinterpret_cast<uint4 *>(&xs[buf][row * BK + swz(row, c) * 16]) = S.x[it];
-            }
+        for (int it = 0; it < WIT4; ++it) {
+            const int c = (tid + it * NW * 64) & 3;
+            const bool ok = kb0 + c * 16 < wrow;
+            w4r[it] = *reinterpret_cast<const uint4 *>(wb + w4off[it] + (ok ? kb0 : wrow - 16 - c * 16));
         }
+    };
+    auto w4_store = [&](auto B) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < WIT; ++it) {
-            const int q = tid + it * NT;
-            if (WCH % NT == 0 || q < WCH) {
-                if constexpr (T::int4) {
-                    const int row = q >> 2, c = q & 3;    // packed chunk c -> int8 chunks 2c, 2c+1
-                    const uint2 a = unpack_int4x8(S.w[it].x), b = unpack_int4x8(S.w[it].y);
-                    const uint2 d = unpack_int4x8(S.w[it].z), e = unpack_int4x8(S.w[it].w);
-                    *reinterpret_cast<uint4 *>(&ws[buf][row * BK + swz(row, 2 * c) * 16]) =
-                        make_uint4(a.x, a.y, b.x, b.y);
-                    *reinterpret_cast<uint4 *>(&ws[buf][row * BK + swz(row, 2 * c + 1) * 16]) =
-                        make_uint4(d.x, d.y, e.x, e.y);
-                } else {
-                    const int row = q >> 3, c = q & 7;
-                    *reinterpret_cast<uint4 *>(&ws[buf][row * BK + swz(row, c) * 16]) = S.w[it];
-                }
-            }
-        }
-        if constexpr (T::fold_sa) {
-            if (tid < BM) {
-#pragma unroll
-                for (int g = 0; g < NG; ++g)
-                    sas[buf][g * BM + tid] = S.sa[g];
-            }
-        }
-        if constexpr (T::fold_sw) {
-            if (tid < BN) {
-#pragma unroll
-                for (int g = 0; g < NG; ++g)
-                    sws[buf][g * BN + tid] = S.sw[g];
+        for (int it = 0; it < WIT4; ++it) {
+            const int q = tid + it * NW * 64;
+            if (WCH4 % (NW * 64) == 0 || q < WCH4) {
+                const int row = q >> 2, c = q & 3;    // packed chunk c -> int8 chunks 2c, 2c+1
+                const uint2 a = unpack_int4x8(w4r[it].x), b = unpack_int4x8(w4r[it].y);
+                const uint2 d = unpack_int4x8(w4r[it].z), e = unpack_int4x8(w4r[it].w);
+                *reinterpret_cast<uint4 *>(WS(B) + row * BK + swz(row, 2 * c) * 16) =
+                    make_uint4(a.x, a.y, b.x, b.y);
+                *reinterpret_cast<uint4 *>(WS(B) + row * BK + swz(row, 2 * c + 1) * 16) =
+                    make_uint4(d.x, d.y, e.x, e.y);
             }
         }
     };
 
-    // ---- accumulators
-    v4i acc[FN][FM];
-    v4f accf[T::fold_sw ? FN : 1][T::fold_sw ? FM : 1];
-    const v4i zero = {0, 0, 0, 0};
+    // ---- accumulators: acc[j][i] is the 32x32 block (n-block j, m-block i)
+    v16i acc[FN][FM];
+    v16f accf[T::fold_sw ? FN : 1][T::fold_sw ? FM : 1];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            acc[j][i] = zero;
+            acc[j][i] = v16i{};
     if constexpr (T::fold_sw) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                accf[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+                accf[j][i] = v16f{};
     }
 
-    // fragment addressing: lane reads row (base + lane%16), logical chunk 4*kk + lane/16
-    const int lrow = lane & 15;
-    const int lchunk = lane >> 4;
-    const int xrow0 = wm * TM + lrow;
-    const int wrow0 = wn * TN + lrow;
-    // output coordinates of this lane inside a 16x16 block
-    const int out_m = lane & 15;
-    const int out_n = (lane >> 4) * 4;
-    // swizzled byte offsets of the lane's fragment chunk for kk = 0, 1 (the
-    // swizzle depends on the row only through lane%16, since bases are multiples of 16)
-    const int xo0 = xrow0 * BK + swz(lrow, lchunk) * 16;
-    const int xo1 = xrow0 * BK + swz(lrow, 4 + lchunk) * 16;
-    const int wo0 = wrow0 * BK + swz(lrow, lchunk) * 16;
-    const int wo1 = wrow0 * BK + swz(lrow, 4 + lchunk) * 16;
+    // Fragment addressing: lane reads row (base + lane%32), logical chunk
+    // 2t + lane/32 for k-step t; bases are multiples of 32, so the swizzle
+    // depends on lane%32 only.
+    const int lrow = lane & 31;
+    const int lhalf = lane >> 5;
+    int fo[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        fo[t] = lrow * BK + swz(lrow, 2 * t + lhalf) * 16;
+    const int xrow0 = wm * TM;
+    const int wrow0 = wn * TN;
+    // output coordinates of this lane inside a 32x32 block: m = lane%32,
+    // n = 8*(r/4) + 4*(lane/32) + r%4 for accumulator element r
+    const int out_m = lane & 31;
+    const int out_n = lhalf * 4;
 
-    auto store_partials = [&](int g) {
+    struct Frag {
+        v4i a[FN];    // weights (A operand)
+        v4i b[FM];    // activations (B operand)
+    };
+    Frag f0, f1;
+
+    auto read_frag = [&](Frag &F, auto B, int t) __attribute__((always_inline)) {
+        const int8_t *xb = XS(B) + xrow0 * BK + fo[t];
+        const int8_t *wbf = WS(B) + wrow0 * BK + fo[t];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            F.b[i] = *reinterpret_cast<const v4i *>(xb + i * 32 * BK);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            F.a[j] = *reinterpret_cast<const v4i *>(wbf + j * 32 * BK);
+    };
+
+    auto mfma_step = [&](const Frag &F, bool restart) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.a[j], F.b[i],
+                                                                  restart ? v16i{} : acc[j][i], 0, 0, 0);
+    };
+
+    auto store_partials = [&](int g) __attribute__((always_inline)) {
         int32_t *P = static_cast<int32_t *>(args.out) + (int64_t)g * M * N;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int m = m0 + wm * TM + i * 16 + out_m;
+            const int m = m0 + wm * TM + i * 32 + out_m;
             if (m >= M)
                 continue;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = n0 + wn * TN + j * 16 + out_n;
-                v4i v = acc[j][i];
-                if constexpr (T::int4)
-                    v = v >> 4;                           // exact: the sums are 16 * P
-                int32_t *dst = P + (int64_t)m * N + n;
-                if (n + 3 < N && (N & 3) == 0) {
-                    *reinterpret_cast<v4i *>(dst) = v;
-                } else {
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < N)
-                            dst[r] = v[r];
-                }
-            }
-        }
-    };
-
-    auto fold_group = [&](int buf, int g) {
-        float sav[FM];
-        v4f swv[FN];
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * TN + j * 32 + q * 8 + out_n;
+                    v4i v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                             acc[j][i][4 * q + 3]};
+                    if constexpr (T::int4)
+                        v = v >> 4;                       // exact: the sums are 16 * P
+                    int32_t *dst = P + (int64_t)m * N + n;
+                    if (n + 3 < N && (N & 3) == 0) {
+                        *reinterpret_cast<v4i *>(dst) = v;
+                    } else {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            sav[i] = T::fold_sa ? sas[buf][g * BM + wm * TM + i * 16 + out_m] : 1.0f;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            swv[j] = *reinterpret_cast<const v4f *>(&sws[buf][g * BN + wn * TN + j * 16 + out_n]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float sc = T::fold_sa ? sav[i] * swv[j][r] : swv[j][r];
-                    accf[j][i][r] = fmaf((float)acc[j][i][r], sc, accf[j][i][r]);
-                }
-    };
-
-    // One 64-wide k step from LDS buffer `buf`.
-    auto mma_step = [&](int buf, int kk, bool restart) {
-        const int8_t *xb = xs[buf];
-        const int8_t *wbuf = ws[buf];
-        const int xo = kk ? xo1 : xo0, wo = kk ? wo1 : wo0;
-        v4i bf[FM], af[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            bf[i] = *reinterpret_cast<const v4i *>(xb + xo + i * 16 * BK);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            af[j] = *reinterpret_cast<const v4i *>(wbuf + wo + j * 16 * BK);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[j], bf[i],
-                                                                  restart ? zero : acc[j][i], 0, 0, 0);
-    };
-
-    auto compute_stage = [&](int buf, int s) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int kc = s * 2 + kk;
-            if (kc < nkc) {
-                // per-group modes start every group from zero
-                mma_step(buf, kk, T::pergroup && (GS == 64 || kk == 0));
-                if constexpr (T::pergroup) {
-                    if (GS == 64 || kk == 1 || kc + 1 == nkc) {
-                        const int g = (GS == 64) ? kc : s;
-                        if constexpr (T::partials)
-                            store_partials(g);
-                        else
-                            fold_group(buf, (GS == 64) ? kk : 0);
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < N)
+                                dst[r] = v[r];
                     }
                 }
+        }
+    };
+
+    auto fold_group = [&](auto B, int g) __attribute__((always_inline)) {
+        float sav[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            sav[i] = T::fold_sa ? SAS(B)[g * BM + wm * TM + i * 32 + out_m] : 1.0f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v4f swv = *reinterpret_cast<const v4f *>(
+                    &SWS(B)[g * BN + wn * TN + j * 32 + q * 8 + out_n]);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float sc = T::fold_sa ? sav[i] * swv[r] : swv[r];
+                        accf[j][i][4 * q + r] =
+                            fmaf((float)acc[j][i][4 * q + r], sc, accf[j][i][4 * q + r]);
+                    }
+            }
+    };
+
+    // After k-step t of stage s: close a group if one ends here.
+    auto after_step = [&](auto B, int s, int t) __attribute__((always_inline)) {
+        if constexpr (T::pergroup) {
+            const int ks = s * 4 + t;
+            if ((t + 1) % SPG == 0 || ks + 1 == nks) {
+                const int gl = t / SPG;                   // group slot within the stage
+                if constexpr (T::partials)
+                    store_partials(s * NG + gl);
+                else
+                    fold_group(B, gl);
             }
         }
     };
 
-    // ---- pipeline.  Stage s is computed from LDS buffer s&1.  Without fp32
-    // accumulators (per-channel) two register sets keep the loads of stages
-    // s+1 and s+2 in flight; the per-group modes, which hold fp32
-    // accumulators too, keep one stage in flight to stay within registers.
-    if constexpr (!T::pergroup) {
-        load_stage(st0, 0);
-        if (nstage > 1)
-            load_stage(st1, 1);
-        store_stage(st0, 0);
+    // ---- pipeline.  Stage t lives in LDS buffer t % 3.  Its copies are
+    // issued during step 3 of iteration t-3 (int4 weights: loaded into
+    // registers in iteration t-2 and unpacked to LDS before the barrier of
+    // iteration t-1).  Iteration s: steps 0-2 from buffer s%3; wait for
+    // stage s+1's copies and barrier; issue stage s+3's copies into buffer
+    // s%3 (nobody reads it any more); step 3, which also reads the first
+    // fragments of stage s+1.  Every iteration issues the same memory
+    // operations -- past the last stage the copies repeat the last stage
+    // into a buffer nobody reads -- so the loop has no branches around them
+    // and every wait count is a constant.
+    const int last = nstage - 1;
+    auto main_loop = [&](auto KFULL) __attribute__((always_inline)) {
+        constexpr bool kfull = decltype(KFULL)::value;   // K % 128 == 0: every k-step exists
+        dma_stage(std::integral_constant<int, 0>(), 0);
+        if constexpr (T::int4) {
+            w4_load(0);
+            w4_store(std::integral_constant<int, 0>());
+            w4_load(min(1, last));
+        }
+        dma_stage(std::integral_constant<int, 1>(), min(1, last));
+        dma_stage(std::integral_constant<int, 2>(), min(2, last));
+        wait_vmcnt<2 * ND>();
         lds_barrier();
-        auto iteration = [&](auto P, int s) {
-            constexpr int p = decltype(P)::value;
-            Stage &cur = p == 0 ? st0 : st1;    // held stage s (already in LDS)
-            Stage &nxt = p == 0 ? st1 : st0;    // holds stage s+1
-            if (s + 2 < nstage)
-                load_stage(cur, s + 2);
-            compute_stage(p, s);
-            if (s + 1 < nstage)
-                store_stage(nxt, p ^ 1);
+        read_frag(f0, std::integral_constant<int, 0>(), 0);
+
+        auto iteration = [&](auto B, int s) __attribute__((always_inline)) {
+            constexpr int b = decltype(B)::value;
+            constexpr int b1 = (b + 1) % 3;
+            const int ks0 = s * 4;
+            auto step = [&](auto TC) __attribute__((always_inline)) {
+                constexpr int t = decltype(TC)::value;
+                Frag &cur = (t & 1) ? f1 : f0;
+                Frag &nxt = (t & 1) ? f0 : f1;
+                if (kfull || ks0 + t < nks) {
+                    if constexpr (t < 3) {
+                        if (kfull || ks0 + t + 1 < nks)
+                            read_frag(nxt, B, t + 1);
+                    } else {
+                        read_frag(nxt, std::integral_constant<int, b1>(), 0);
+                    }
+                    // keep the reads for the next step ahead of this step's
+                    // MFMAs, which use fragments read one step earlier
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_step(cur, T::pergroup && (t % SPG == 0));
+                    __builtin_amdgcn_sched_barrier(0);
+                    after_step(B, s, t);
+                }
+            };
+            step(std::integral_constant<int, 0>());
+            step(std::integral_constant<int, 1>());
+            step(std::integral_constant<int, 2>());
+            // stage s+1 complete and visible; buffer b free
+            if constexpr (T::int4)
+                w4_store(std::integral_constant<int, b1>());
+            wait_vmcnt<ND>();
             lds_barrier();
+            if constexpr (T::int4)
+                w4_load(min(s + 2, last));
+            if constexpr (T::fold_sw) {
+                // the fold after step 3 still reads this stage's scales from
+                // buffer b: copy into it only afterwards
+                step(std::integral_constant<int, 3>());
+                dma_stage(B, min(s + 3, last));
+            } else {
+                dma_stage(B, min(s + 3, last));
+                step(std::integral_constant<int, 3>());
+            }
         };
-        for (int s = 0; s < nstage; s += 2) {
+        for (int s = 0; s < nstage; s += 3) {
             iteration(std::integral_constant<int, 0>(), s);
-            if (s + 1 < nstage)
+            if (s + 1 < nstage) {
                 iteration(std::integral_constant<int, 1>(), s + 1);
+                if (s + 2 < nstage)
+                    iteration(std::integral_constant<int, 2>(), s + 2);
+            }
         }
-    } else {
-        load_stage(st0, 0);
-        store_stage(st0, 0);
-        lds_barrier();
-        for (int s = 0; s < nstage; ++s) {
-            if (s + 1 < nstage)
-                load_stage(st0, s + 1);
-            compute_stage(s & 1, s);
-            if (s + 1 < nstage)
-                store_stage(st0, (s + 1) & 1);
-            lds_barrier();
-        }
-    }
+        // no copy may still be writing LDS when the workgroup ends
+        wait_vmcnt<0>();
+    };
+    if (K % BK == 0)
+        main_loop(std::true_type());
+    else
+        main_loop(std::false_type());
 
     // ---- epilogue
     if constexpr (T::partials) {
@@ -409,66 +510,75 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         int32_t *C = static_cast<int32_t *>(args.out);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int m = m0 + wm * TM + i * 16 + out_m;
+            const int m = m0 + wm * TM + i * 32 + out_m;
             if (m >= M)
                 continue;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = n0 + wn * TN + j * 16 + out_n;
-                int32_t *dst = C + (int64_t)m * N + n;
-                if (n + 3 < N && (N & 3) == 0) {
-                    *reinterpret_cast<v4i *>(dst) = acc[j][i];
-                } else {
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < N)
-                            dst[r] = acc[j][i][r];
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * TN + j * 32 + q * 8 + out_n;
+                    const v4i v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                                   acc[j][i][4 * q + 3]};
+                    int32_t *dst = C + (int64_t)m * N + n;
+                    if (n + 3 < N && (N & 3) == 0) {
+                        *reinterpret_cast<v4i *>(dst) = v;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < N)
+                                dst[r] = v[r];
+                    }
                 }
-            }
         }
     } else {
         uint16_t *Y = static_cast<uint16_t *>(args.out);
-        v4f swv[FN];
-        if constexpr (MODE == GemmMode::PC) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = n0 + wn * TN + j * 16 + out_n;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    swv[j][r] = args.sw[min(n + r, N - 1)];
-            }
-        }
         const bool vec_ok = (N & 3) == 0;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int m = m0 + wm * TM + i * 16 + out_m;
+            const int m = m0 + wm * TM + i * 32 + out_m;
             if (m >= M)
                 continue;
             const float sa = (MODE == GemmMode::PG) ? 1.0f : args.sa[m];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = n0 + wn * TN + j * 16 + out_n;
-                float v[4];
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (MODE == GemmMode::PC)
-                        v[r] = rescale_pc(acc[j][i][r], sa, swv[j][r]);
-                    else if constexpr (MODE == GemmMode::PG)
-                        v[r] = accf[j][i][r];
-                    else
-                        v[r] = accf[j][i][r] * sa;     // W4: per-token scale last
-                }
-                uint16_t *dst = Y + (int64_t)m * N + n;
-                if (vec_ok && n + 3 < N) {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_h2(v[0], v[1]),
-                                                                 pack_h2(v[2], v[3]));
-                } else {
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * TN + j * 32 + q * 8 + out_n;
+                    float v[4];
+                    if constexpr (MODE == GemmMode::PC) {
+                        float swq[4];
+                        if (vec_ok && n + 3 < N) {
+                            const float4 t4 = *reinterpret_cast<const float4 *>(args.sw + n);
+                            swq[0] = t4.x; swq[1] = t4.y; swq[2] = t4.z; swq[3] = t4.w;
+                        } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < N)
-                            dst[r] = f2h(v[r]);
+                            for (int r = 0; r < 4; ++r)
+                                swq[r] = args.sw[min(n + r, N - 1)];
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] = rescale_pc(acc[j][i][4 * q + r], sa, swq[r]);
+                    } else if constexpr (MODE == GemmMode::PG) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] = accf[j][i][4 * q + r];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] = accf[j][i][4 * q + r] * (sa * 0.0625f);   // W4: per-token scale, undo x16 (exact)
+                    }
+                    uint16_t *dst = Y + (int64_t)m * N + n;
+                    if (vec_ok && n + 3 < N) {
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_h2(v[0], v[1]),
+                                                                     pack_h2(v[2], v[3]));
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < N)
+                                dst[r] = f2h(v[r]);
+                    }
                 }
-            }
         }
     }
 }
@@ -484,30 +594,37 @@ void launch_cfg(const GemmArgs &a, hipStream_t st)
 }
 
 // Pick a tile shape: large tiles when the output is big, smaller ones when
-// too few tiles would leave compute units idle.
+// too few tiles would leave compute units idle.  The per-group modes hold
+// fp32 accumulators next to the int32 ones and stay at 128x128 or below.
 template <GemmMode MODE, int GS>
 void launch_mode(const GemmArgs &a, hipStream_t st)
 {
-    constexpr bool wide_ok = !ModeTraits<MODE>::pergroup;   // 256x160 only without fp32 accumulators
+    constexpr bool pergroup = ModeTraits<MODE>::pergroup;
     const int64_t t256x160 = (int64_t)((a.M + 255) / 256) * ((a.N + 159) / 160);
     const int64_t t256x128 = (int64_t)((a.M + 255) / 256) * ((a.N + 127) / 128);
     const int64_t t128x128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-    if (a.M <= 64) {
-        launch_cfg<64, 64, 1, 4, MODE, GS>(a, st);
+    if (a.M <= 32) {
+        launch_cfg<32, 128, 1, 4, MODE, GS>(a, st);
         return;
     }
-    if constexpr (wide_ok) {
+    if (a.M <= 64) {
+        launch_cfg<64, 128, 2, 2, MODE, GS>(a, st);
+        return;
+    }
+    if constexpr (!pergroup) {
         if (t256x160 >= 512 && a.N % 160 == 0) {
-            launch_cfg<256, 160, 2, 2, MODE, GS>(a, st);
+            launch_cfg<256, 160, 4, 1, MODE, GS>(a, st);
+            return;
+        }
+        if (t256x128 >= 512) {
+            launch_cfg<256, 128, 2, 2, MODE, GS>(a, st);
             return;
         }
     }
-    if (t256x128 >= 512)
-        launch_cfg<256, 128, 2, 2, MODE, GS>(a, st);
-    else if (t128x128 >= 256)
+    if (t128x128 >= 256)
         launch_cfg<128, 128, 2, 2, MODE, GS>(a, st);
     else
-        launch_cfg<128, 64, 2, 2, MODE, GS>(a, st);
+        launch_cfg<64, 128, 2, 2, MODE, GS>(a, st);
 }
 
 }  // namespace
