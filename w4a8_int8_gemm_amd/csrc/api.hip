@@ -33,26 +33,33 @@ w4a8_status_t ok()
 constexpr int64_t kMaxDim = 0x7fffffff;
 constexpr int64_t kMaxKPerChannel = 133144;   // largest K with 127^2 * K < 2^31
 constexpr int64_t kMaxKMv = 32768;            // the token's codes are staged in LDS
+constexpr int64_t kMaxKGemm = int64_t(1) << 22; // a 256-row tile of K bytes stays below 2^30
+constexpr int64_t kMaxTiles = 0x7fffffff;     // 32 x 128 output tiles
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-// 1 = gfx950, 0 = other, -1 = not yet known; per device ordinal.
-std::atomic<int> g_arch_ok[64];
-struct ArchInit {
-    ArchInit() { for (auto &a : g_arch_ok) a.store(-1); }
-} g_arch_init;
+// Per device ordinal: its compute-unit count if it is a gfx950, 0 if it is
+// something else, -1 while not yet known.
+std::atomic<int> g_dev_cu[64];
+struct DevInit {
+    DevInit() { for (auto &a : g_dev_cu) a.store(-1); }
+} g_dev_init;
 
-w4a8_status_t check_device()
+// The current device must be a gfx950; *num_cu receives its compute units.
+w4a8_status_t check_device(int *num_cu = nullptr)
 {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess || dev < 0)
         return fail(W4A8_ERR_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
     if (dev < 64) {
-        int known = g_arch_ok[dev].load(std::memory_order_relaxed);
-        if (known == 1)
+        const int known = g_dev_cu[dev].load(std::memory_order_relaxed);
+        if (known > 0) {
+            if (num_cu)
+                *num_cu = known;
             return W4A8_OK;
+        }
         if (known == 0)
             return fail(W4A8_ERR_DEVICE, "HIP device %d is not gfx950", dev);
     }
@@ -61,10 +68,13 @@ w4a8_status_t check_device()
     if (e != hipSuccess)
         return fail(W4A8_ERR_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
     const bool is950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    const int cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
     if (dev < 64)
-        g_arch_ok[dev].store(is950 ? 1 : 0, std::memory_order_relaxed);
+        g_dev_cu[dev].store(is950 ? cus : 0, std::memory_order_relaxed);
     if (!is950)
         return fail(W4A8_ERR_DEVICE, "HIP device %d is %s, not gfx950", dev, prop.gcnArchName);
+    if (num_cu)
+        *num_cu = cus;
     return W4A8_OK;
 }
 
@@ -120,6 +130,12 @@ w4a8_status_t check_gemm(const char *fn, const void *xq, const void *w, const vo
         return fail(W4A8_ERR_SHAPE, "%s: K=%lld could overflow the int32 sums (max %lld)", fn,
                     (long long)K, (long long)kMaxKPerChannel);
     }
+    if (K > kMaxKGemm)
+        return fail(W4A8_ERR_SHAPE, "%s: K=%lld exceeds %lld", fn, (long long)K,
+                    (long long)kMaxKGemm);
+    if (((M + 31) / 32) * ((N + 127) / 128) > kMaxTiles)
+        return fail(W4A8_ERR_SHAPE, "%s: output of %lld x %lld is too large", fn, (long long)M,
+                    (long long)N);
     if (M == 0 || N == 0)
         return W4A8_OK;
     if (!xq || !w || !out || (need_scales && (!sa || !sw)))
@@ -156,6 +172,7 @@ GemmArgs make_args(const int8_t *xq, const float *sa, const void *w, const float
     GemmArgs a;
     a.xq = xq; a.sa = sa; a.w = w; a.sw = sw; a.out = out;
     a.M = (int)M; a.N = (int)N; a.K = (int)K; a.gs = gs;
+    a.num_cu = 1;
     return a;
 }
 
@@ -163,10 +180,11 @@ w4a8_status_t run_gemm(const char *fn, GemmMode mode, const GemmArgs &a, w4a8_st
 {
     if (a.M == 0 || a.N == 0)
         return ok();
-    w4a8_status_t st = check_device();
+    GemmArgs la = a;
+    w4a8_status_t st = check_device(&la.num_cu);
     if (st != W4A8_OK)
         return st;
-    launch_gemm(mode, a, (hipStream_t)stream);
+    launch_gemm(mode, la, (hipStream_t)stream);
     return check_launch(fn);
 }
 

@@ -60,6 +60,17 @@ __device__ __forceinline__ uint2 unpack_int4x8(uint32_t x)
     return make_uint2(a, b);
 }
 
+// Output pairs.  Each lane holds, for one output column n, the values of two
+// consecutive rows m, m+1 (packed as fp16 lo/hi).  Adjacent lanes (n even,
+// n+1) trade halves so that the even lane holds row m at columns n, n+1 and
+// the odd lane row m+1 at columns n-1, n: one 4-byte store each.
+__device__ __forceinline__ uint32_t pair_rows_to_cols(uint32_t p, uint32_t sel)
+{
+    // the neighbouring lane's pair (quad_perm [1, 0, 3, 2])
+    const uint32_t q = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p, 0xb1, 0xf, 0xf, false);
+    return __builtin_amdgcn_perm(p, q, sel);
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads stay in
 // flight across it (a full __syncthreads would also wait for them).
 __device__ __forceinline__ void lds_barrier()
@@ -118,6 +129,36 @@ template <int N> __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Buffer resource of a raw byte range [base, base + bytes): loads at offsets
+// past `bytes` return zeros instead of touching memory.
+__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));   // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;                                  // gfx9 raw buffer: 32-bit data format
+    return r;
+}
+
+// 16 bytes per lane from a buffer resource into LDS at M0 + 16 * lane.
+__device__ __forceinline__ void copy16_buf_to_lds(v4i rsrc, uint32_t voff, uint32_t lds)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
+// Persistent kernel: the grid holds at most as many workgroups as fit on the
+// device at once, and workgroup b computes the tiles b', b' + G, b' + 2G, ...
+// of a fixed tile order (G = grid size, b' an XCD-contiguous renumbering of
+// b).  Its K-stages form one stream across its tiles, so the copies of the
+// next tile's first stages are in flight while the current tile finishes and
+// writes its outputs.
 template <int BM, int BN, int WM, int WN, GemmMode MODE, int GS>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int tiles_m,
                                                            int tiles_n, int group_m)
@@ -134,6 +175,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     constexpr bool kDmaW = !T::int4;                  // int8 weights go straight to LDS
     constexpr int WB = kDmaW ? WBUF / 1024 / NW : 0;
     static_assert(!kDmaW || WBUF % (1024 * NW) == 0, "W stage must split evenly over the waves");
+    constexpr int RB = XB > WB ? XB : WB;             // distinct row offsets per lane
     // packed int4 weights are staged through registers and unpacked
     constexpr int WCH4 = BN * 4;                      // 16-byte packed chunks per stage
     constexpr int WIT4 = T::int4 ? (WCH4 + NW * 64 - 1) / (NW * 64) : 0;
@@ -143,35 +185,37 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     // NG*BN weight scales, in instructions of 64 lanes, dealt round-robin
     constexpr int SA_I = T::fold_sa ? (NG * BM + 63) / 64 : 0;
     constexpr int SW_I = T::fold_sw ? (NG * BN + 63) / 64 : 0;
-    // copies every wave issues per stage (a lower bound where the scale
-    // instructions do not split evenly; waiting on it is conservative)
+    constexpr int SAW = (SA_I + NW - 1) / NW, SWW = (SW_I + NW - 1) / NW;
+    // copy instructions of one stage, per wave: X blocks, W blocks, then the
+    // scale instructions (which some waves skip where they do not split evenly)
+    constexpr int NCW = XB + WB + SAW + SWW;
+    // copies every wave surely issues per stage (waiting on it is exact or
+    // conservative)
     constexpr int ND = XB + WB + SA_I / NW + SW_I / NW;
+    // The copies of stage u are spread over four k-steps: part A in step 3 of
+    // iteration u-3, parts 0..2 in steps 0..2 of iteration u-2.  Scale copies
+    // never go in part A (the group fold after step 3 still reads the scales
+    // in that buffer).  int4 weights are register-staged; their compiler
+    // tracked loads make it wait for every earlier copy before the unpack, so
+    // there the tile copies all go in part A and the scale copies in part 0.
+    constexpr int NCP = NCW / 4, NCR = NCW % 4;
+    constexpr int CA = T::int4 ? XB + WB : NCP + (NCR > 0);
+    constexpr int C0 = T::int4 ? NCW - CA : NCP + (NCR > 1);
+    constexpr int C1 = T::int4 ? 0 : NCP + (NCR > 2);
+    constexpr int C2 = T::int4 ? 0 : NCP;
+    static_assert(CA + C0 + C1 + C2 == NCW, "copy split");
+    static_assert(!T::pergroup || CA <= XB + WB, "scale copies must not go in part A");
+    // epilogue scales staged in LDS: per-token sa (PC, W4) followed by
+    // per-channel sw (PC)
+    constexpr int ESN = (MODE == GemmMode::PC) ? BM + BN : (MODE == GemmMode::W4 ? BM : 0);
+    constexpr int EW = (ESN + 64 * NW - 1) / (64 * NW);   // copy instructions per wave
 
-    __shared__ __attribute__((aligned(1024))) int8_t xs0[XBUF];
-    __shared__ __attribute__((aligned(1024))) int8_t xs1[XBUF];
-    __shared__ __attribute__((aligned(1024))) int8_t xs2[XBUF];
-    __shared__ __attribute__((aligned(1024))) int8_t ws0[WBUF];
-    __shared__ __attribute__((aligned(1024))) int8_t ws1[WBUF];
-    __shared__ __attribute__((aligned(1024))) int8_t ws2[WBUF];
+    __shared__ __attribute__((aligned(1024))) int8_t xs[3 * XBUF];
+    __shared__ __attribute__((aligned(1024))) int8_t ws[3 * WBUF];
     constexpr int SAL = T::fold_sa ? NG * BM : 1, SWL = T::fold_sw ? NG * BN : 1;
-    __shared__ __attribute__((aligned(16))) float sa0[SAL], sa1[SAL], sa2[SAL];
-    __shared__ __attribute__((aligned(16))) float sw0[SWL], sw1[SWL], sw2[SWL];
-    auto XS = [&](auto B) __attribute__((always_inline)) -> int8_t * {
-        constexpr int b = decltype(B)::value;
-        return b == 0 ? xs0 : (b == 1 ? xs1 : xs2);
-    };
-    auto WS = [&](auto B) __attribute__((always_inline)) -> int8_t * {
-        constexpr int b = decltype(B)::value;
-        return b == 0 ? ws0 : (b == 1 ? ws1 : ws2);
-    };
-    auto SAS = [&](auto B) __attribute__((always_inline)) -> float * {
-        constexpr int b = decltype(B)::value;
-        return b == 0 ? sa0 : (b == 1 ? sa1 : sa2);
-    };
-    auto SWS = [&](auto B) __attribute__((always_inline)) -> float * {
-        constexpr int b = decltype(B)::value;
-        return b == 0 ? sw0 : (b == 1 ? sw1 : sw2);
-    };
+    __shared__ __attribute__((aligned(16))) float sas[T::fold_sa ? 3 * SAL : 1];
+    __shared__ __attribute__((aligned(16))) float sws[T::fold_sw ? 3 * SWL : 1];
+    __shared__ __attribute__((aligned(16))) float eps[EW > 0 ? EW * NW * 64 : 1];
 
     const int M = args.M, N = args.N, K = args.K;
     const int tid = threadIdx.x;
@@ -179,108 +223,155 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    // ---- tile selection: XCD-contiguous ranges, grouped along m
-    int tm, tn;
+    // ---- this workgroup's tiles.  Workgroups are dealt to the XCDs round
+    // robin; renumber them so each XCD holds a contiguous range, and order the
+    // tiles in groups of group_m tile rows, so that the tiles in flight on one
+    // XCD (one L2) share rows of X and of W.
+    const int G = (int)gridDim.x;
+    int wl;
     {
-        const int nb = (int)gridDim.x, bid = (int)blockIdx.x;
+        const int bid = (int)blockIdx.x;
         const int xcd = bid & 7, local = bid >> 3;
-        const int per = nb >> 3, rem = nb & 7;
-        const int lid = (xcd < rem) ? xcd * (per + 1) + local
-                                    : rem * (per + 1) + (xcd - rem) * per + local;
+        const int per = G >> 3, rem = G & 7;
+        wl = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+    }
+    const int total = tiles_m * tiles_n;
+    const int ntile = (total - wl + G - 1) / G;       // >= 1: the grid has at most `total` groups
+    auto tile_origin = [&](int i, int &m0, int &n0) __attribute__((always_inline)) {
+        const int lid = i * G + wl;
         const int span = group_m * tiles_n;
         const int first_m = (lid / span) * group_m;
         const int gm = min(tiles_m - first_m, group_m);
         const int in = lid % span;
-        tm = first_m + in % gm;
-        tn = in / gm;
-    }
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int G = T::pergroup ? K / GS : 1;
+        m0 = (first_m + in % gm) * BM;
+        n0 = (in / gm) * BN;
+    };
+    const int G_ = T::pergroup ? K / GS : 1;          // groups along K
     const int nstage = (K + BK - 1) / BK;
     const int nks = K / 32;                           // 32-wide MFMA steps in K
+    const int U = ntile * nstage;                     // stages this workgroup computes
 
     const int8_t *__restrict__ xq = args.xq;
     const uint8_t *__restrict__ wb = static_cast<const uint8_t *>(args.w);
     const int wrow = T::int4 ? K / 2 : K;             // bytes per weight row
 
-    // Direct-to-LDS source offsets.  A wave instruction writes lane l's 16
-    // bytes at LDS block + 16*l, i.e. row 8*blk + l/8, physical chunk l%8; the
-    // lane therefore fetches the logical chunk that the swizzle puts there.
+    // Direct-to-LDS copies.  A wave instruction writes lane l's 16 bytes at
+    // LDS block + 16*l, i.e. row 8*blk + l/8, physical chunk l%8; the lane
+    // therefore fetches the logical chunk that the swizzle puts there.  Byte
+    // offsets within a tile (X and int8 W rows are both K bytes long); rows
+    // past the end of the matrix fall outside the tile's buffer resource and
+    // read as zeros.
     const int dma_row = lane >> 3;
     const int dma_chunk = (lane & 7) ^ (dma_row & 7);
-    int64_t xoff[XB];
+    uint32_t vrow[RB];
 #pragma unroll
-    for (int i = 0; i < XB; ++i) {
-        const int row = (wave + NW * i) * 8 + dma_row;
-        xoff[i] = (int64_t)min(m0 + row, M - 1) * K + dma_chunk * 16;
-    }
-    int64_t woff[WB > 0 ? WB : 1];
-#pragma unroll
-    for (int i = 0; i < WB; ++i) {
-        const int row = (wave + NW * i) * 8 + dma_row;
-        woff[i] = (int64_t)min(n0 + row, N - 1) * K + dma_chunk * 16;
-    }
-    // packed int4 weights: thread -> (row, 16-byte packed chunk)
-    int64_t w4off[WIT4 > 0 ? WIT4 : 1];
-#pragma unroll
-    for (int it = 0; it < WIT4; ++it) {
-        const int q = min(tid + it * NW * 64, WCH4 - 1);
-        w4off[it] = (int64_t)min(n0 + (q >> 2), N - 1) * wrow + (q & 3) * 16;
-    }
+    for (int i = 0; i < RB; ++i)
+        vrow[i] = (uint32_t)(((wave + NW * i) * 8 + dma_row) * K + dma_chunk * 16);
 
-    // Issue the copies of stage s into LDS buffer B.
-    auto dma_stage = [&](auto B, int s) __attribute__((always_inline)) {
-        const int k0 = s * BK;
-        const bool full = k0 + BK <= K;               // else: K % 128 == 64, upper half unused
-        const int kx = (full || k0 + dma_chunk * 16 < K) ? k0 : K - 16 - dma_chunk * 16;
-#pragma unroll
-        for (int i = 0; i < XB; ++i)
-            copy16_to_lds(xq + xoff[i] + kx, lds_addr(XS(B) + (wave + NW * i) * 1024));
-#pragma unroll
-        for (int i = 0; i < WB; ++i)
-            copy16_to_lds(wb + woff[i] + kx, lds_addr(WS(B) + (wave + NW * i) * 1024));
-        if constexpr (T::fold_sa) {
-#pragma unroll
-            for (int i = 0; i < (SA_I + NW - 1) / NW; ++i) {
-                const int ins = wave + NW * i;
+    // Where the copies of one stage come from: the stage's tile, its index
+    // within the tile and the LDS buffer it goes to.  Wave-uniform.
+    struct Src {
+        int v;         // stage in this workgroup's stream (clamped to U - 1)
+        int s;         // stage within its tile
+        int tile;      // tile within this workgroup's list
+        int buf;       // LDS buffer (the unclamped stage index mod 3)
+        int m0, n0;    // tile origin
+        v4i rx, rw;    // buffer resources of the tile's X rows and int8 W rows
+    };
+    auto set_tile = [&](Src &c, int i) __attribute__((always_inline)) {
+        c.tile = i;
+        tile_origin(i, c.m0, c.n0);
+        c.rx = make_rsrc(xq + (int64_t)c.m0 * K, (uint32_t)(min(BM, M - c.m0) * K));
+        if constexpr (kDmaW)
+            c.rw = make_rsrc(wb + (int64_t)c.n0 * K, (uint32_t)(min(BN, N - c.n0) * K));
+    };
+    auto advance = [&](Src &c) __attribute__((always_inline)) {
+        c.buf = c.buf == 2 ? 0 : c.buf + 1;
+        if (c.v + 1 < U) {                            // past the end: repeat the last stage
+            ++c.v;
+            if (++c.s == nstage) {
+                c.s = 0;
+                set_tile(c, c.tile + 1);
+            }
+        }
+    };
+
+    // Copy c (0 <= c < NCW) of the stage described by `src`.  c is a
+    // constant once the callers' loops are unrolled.
+    auto issue_copy = [&](const Src &src, int c) __attribute__((always_inline)) {
+        const uint32_t k0 = (uint32_t)(src.s * BK);
+        if (c < XB) {
+            copy16_buf_to_lds(src.rx, vrow[c] + k0,
+                              lds_addr(xs + src.buf * XBUF + (wave + NW * c) * 1024));
+        } else if (c < XB + WB) {
+            const int i = c - XB;
+            copy16_buf_to_lds(src.rw, vrow[i] + k0,
+                              lds_addr(ws + src.buf * WBUF + (wave + NW * i) * 1024));
+        } else if (c < XB + WB + SAW) {
+            if constexpr (T::fold_sa) {
+                const int ins = wave + NW * (c - XB - WB);
                 if (SA_I % NW == 0 || ins < SA_I) {
                     const int e = ins * 64 + lane;    // entry g*BM + r
                     const int g = min(e / BM, NG - 1), r = e % BM;
-                    const int gi = min(s * NG + g, G - 1);
+                    const int gi = min(src.s * NG + g, G_ - 1);
                     if (e < NG * BM)
-                        copy4_to_lds(args.sa + (int64_t)min(m0 + r, M - 1) * G + gi,
-                                     lds_addr(SAS(B) + ins * 64));
+                        copy4_to_lds(args.sa + (int64_t)min(src.m0 + r, M - 1) * G_ + gi,
+                                     lds_addr(sas + src.buf * SAL + ins * 64));
                 }
             }
-        }
-        if constexpr (T::fold_sw) {
-#pragma unroll
-            for (int i = 0; i < (SW_I + NW - 1) / NW; ++i) {
-                const int ins = wave + NW * i;
+        } else {
+            if constexpr (T::fold_sw) {
+                const int ins = wave + NW * (c - XB - WB - SAW);
                 if (SW_I % NW == 0 || ins < SW_I) {
                     const int e = ins * 64 + lane;    // entry g*BN + r
                     const int g = min(e / BN, NG - 1), r = e % BN;
-                    const int gi = min(s * NG + g, G - 1);
+                    const int gi = min(src.s * NG + g, G_ - 1);
                     if (e < NG * BN)
-                        copy4_to_lds(args.sw + (int64_t)min(n0 + r, N - 1) * G + gi,
-                                     lds_addr(SWS(B) + ins * 64));
+                        copy4_to_lds(args.sw + (int64_t)min(src.n0 + r, N - 1) * G_ + gi,
+                                     lds_addr(sws + src.buf * SWL + ins * 64));
                 }
             }
+        }
+    };
+    // Copies [c0, c0 + n) of a stage, back to back.
+    auto issue_copies = [&](const Src &src, int c0, int n) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NCW; ++c)
+            if (c >= c0 && c < c0 + n)
+                issue_copy(src, c);
+    };
+    // The epilogue scales of the tile at (m0, n0); rows and columns past the
+    // end repeat the last one.
+    auto issue_epilogue_scales = [&](int m0, int n0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < EW; ++i) {
+            const int e = (wave + NW * i) * 64 + lane;
+            const float *src;
+            if (e < BM)
+                src = args.sa + min(m0 + e, M - 1);
+            else if (MODE == GemmMode::PC && e < BM + BN)
+                src = args.sw + min(n0 + e - BM, N - 1);
+            else
+                src = args.sa + min(m0, M - 1);        // padding slot, never read
+            copy4_to_lds(src, lds_addr(eps + (wave + NW * i) * 64));
         }
     };
 
     // ---- packed int4 weights: register staging and unpack into LDS
     uint4 w4r[WIT4 > 0 ? WIT4 : 1];
-    auto w4_load = [&](int s) __attribute__((always_inline)) {
-        const int kb0 = s * (BK / 2);
+    auto w4_load = [&](const Src &src) __attribute__((always_inline)) {
+        const int kb0 = src.s * (BK / 2);
 #pragma unroll
         for (int it = 0; it < WIT4; ++it) {
-            const int c = (tid + it * NW * 64) & 3;
+            const int q = min(tid + it * NW * 64, WCH4 - 1);
+            const int c = q & 3;
             const bool ok = kb0 + c * 16 < wrow;
-            w4r[it] = *reinterpret_cast<const uint4 *>(wb + w4off[it] + (ok ? kb0 : wrow - 16 - c * 16));
+            const int64_t off = (int64_t)min(src.n0 + (q >> 2), N - 1) * wrow + c * 16;
+            w4r[it] = *reinterpret_cast<const uint4 *>(wb + off + (ok ? kb0 : wrow - 16 - c * 16));
         }
     };
-    auto w4_store = [&](auto B) __attribute__((always_inline)) {
+    auto w4_store = [&](int buf) __attribute__((always_inline)) {
+        int8_t *W = ws + buf * WBUF;
 #pragma unroll
         for (int it = 0; it < WIT4; ++it) {
             const int q = tid + it * NW * 64;
@@ -288,9 +379,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                 const int row = q >> 2, c = q & 3;    // packed chunk c -> int8 chunks 2c, 2c+1
                 const uint2 a = unpack_int4x8(w4r[it].x), b = unpack_int4x8(w4r[it].y);
                 const uint2 d = unpack_int4x8(w4r[it].z), e = unpack_int4x8(w4r[it].w);
-                *reinterpret_cast<uint4 *>(WS(B) + row * BK + swz(row, 2 * c) * 16) =
+                *reinterpret_cast<uint4 *>(W + row * BK + swz(row, 2 * c) * 16) =
                     make_uint4(a.x, a.y, b.x, b.y);
-                *reinterpret_cast<uint4 *>(WS(B) + row * BK + swz(row, 2 * c + 1) * 16) =
+                *reinterpret_cast<uint4 *>(W + row * BK + swz(row, 2 * c + 1) * 16) =
                     make_uint4(d.x, d.y, e.x, e.y);
             }
         }
@@ -304,13 +395,16 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             acc[j][i] = v16i{};
-    if constexpr (T::fold_sw) {
+    auto clear_accf = [&]() __attribute__((always_inline)) {
+        if constexpr (T::fold_sw) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                accf[j][i] = v16f{};
-    }
+                for (int i = 0; i < FM; ++i)
+                    accf[j][i] = v16f{};
+        }
+    };
+    clear_accf();
 
     // Fragment addressing: lane reads row (base + lane%32), logical chunk
     // 2t + lane/32 for k-step t; bases are multiples of 32, so the swizzle
@@ -323,177 +417,301 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         fo[t] = lrow * BK + swz(lrow, 2 * t + lhalf) * 16;
     const int xrow0 = wm * TM;
     const int wrow0 = wn * TN;
-    // output coordinates of this lane inside a 32x32 block: m = lane%32,
-    // n = 8*(r/4) + 4*(lane/32) + r%4 for accumulator element r
-    const int out_m = lane & 31;
-    const int out_n = lhalf * 4;
+    // output coordinates of this lane inside a 32x32 block: n = lane%32,
+    // m = 8*(r/4) + 4*(lane/32) + r%4 for accumulator element r
+    const int out_n = lane & 31;
+    const int out_m = lhalf * 4;
+    // byte selector of pair_rows_to_cols: even lanes keep the low halves
+    // (row m), odd lanes the high halves (row m+1)
+    const uint32_t pair_sel = (lane & 1) ? 0x07060302u : 0x01000504u;
 
     struct Frag {
-        v4i a[FN];    // weights (A operand)
-        v4i b[FM];    // activations (B operand)
+        v4i a[FN];    // weights (B operand)
+        v4i b[FM];    // activations (A operand)
     };
     Frag f0, f1;
 
-    auto read_frag = [&](Frag &F, auto B, int t) __attribute__((always_inline)) {
-        const int8_t *xb = XS(B) + xrow0 * BK + fo[t];
-        const int8_t *wbf = WS(B) + wrow0 * BK + fo[t];
+    // Fragment r (0 <= r < FM + FN) of k-step t from buffer buf, in the order
+    // the next step's MFMAs first use them: b[0], a[0], b[1..], a[1..].
+    constexpr int NR = FM + FN;
+    auto read_one = [&](Frag &F, int buf, int t, int r) __attribute__((always_inline)) {
+        const int8_t *xb = xs + buf * XBUF + xrow0 * BK + fo[t];
+        const int8_t *wbf = ws + buf * WBUF + wrow0 * BK + fo[t];
+        if (r == 0)
+            F.b[0] = *reinterpret_cast<const v4i *>(xb);
+        else if (r == 1)
+            F.a[0] = *reinterpret_cast<const v4i *>(wbf);
+        else if (r < FM + 1)
+            F.b[r - 1] = *reinterpret_cast<const v4i *>(xb + (r - 1) * 32 * BK);
+        else
+            F.a[r - FM] = *reinterpret_cast<const v4i *>(wbf + (r - FM) * 32 * BK);
+    };
+    auto read_frag = [&](Frag &F, int buf, int t) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            F.b[i] = *reinterpret_cast<const v4i *>(xb + i * 32 * BK);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            F.a[j] = *reinterpret_cast<const v4i *>(wbf + j * 32 * BK);
+        for (int r = 0; r < NR; ++r)
+            read_one(F, buf, t, r);
     };
 
-    auto mfma_step = [&](const Frag &F, bool restart) __attribute__((always_inline)) {
+    // The MFMAs of one k-step (restarting the sums when RESTART) on F.
+    // Interleaved with them: the fragments of the next step into G (fragment
+    // r after MFMA r * FN * FM / NR, when `reads`), and copies [c0, c0 + n)
+    // of the stage `src` (copy p after MFMA (2p + 1) * FN * FM / (2n)).
+    auto mfma_step = [&](const Frag &F, auto RESTART, Frag &G, bool reads, int rbuf, int rt,
+                         const Src &src, int c0, int n) __attribute__((always_inline)) {
+        constexpr bool restart = decltype(RESTART)::value;
+        constexpr int NM = FN * FM;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int k = 0; k < NM; ++k) {
+            const int j = k / FM, i = k % FM;
+            acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.b[i], F.a[j],
+                                                              restart ? v16i{} : acc[j][i], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (reads) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.a[j], F.b[i],
-                                                                  restart ? v16i{} : acc[j][i], 0, 0, 0);
-    };
-
-    auto store_partials = [&](int g) __attribute__((always_inline)) {
-        int32_t *P = static_cast<int32_t *>(args.out) + (int64_t)g * M * N;
+                for (int r = 0; r < NR; ++r)
+                    if ((r * NM) / NR == k)
+                        read_one(G, rbuf, rt, r);
+            }
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int m = m0 + wm * TM + i * 32 + out_m;
-            if (m >= M)
-                continue;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + wn * TN + j * 32 + q * 8 + out_n;
-                    v4i v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
-                             acc[j][i][4 * q + 3]};
-                    if constexpr (T::int4)
-                        v = v >> 4;                       // exact: the sums are 16 * P
-                    int32_t *dst = P + (int64_t)m * N + n;
-                    if (n + 3 < N && (N & 3) == 0) {
-                        *reinterpret_cast<v4i *>(dst) = v;
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (n + r < N)
-                                dst[r] = v[r];
-                    }
-                }
+            for (int p = 0; p < NCW; ++p)
+                if (p < n && k == ((2 * p + 1) * NM) / (2 * n))
+                    issue_copy(src, c0 + p);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    auto fold_group = [&](auto B, int g) __attribute__((always_inline)) {
-        float sav[FM];
+    // int32 sums of a 32x32 block: per accumulator element one 4-byte store,
+    // lanes 0-31 along one row, 32-63 along the row four below.
+    auto store_block_i32 = [&](int32_t *C, const v16i &blk, int mb, int nb, bool shift4)
+                               __attribute__((always_inline)) {
+        const int n = nb + out_n;
+        if (n >= N)
+            return;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            sav[i] = T::fold_sa ? SAS(B)[g * BM + wm * TM + i * 32 + out_m] : 1.0f;
+        for (int r = 0; r < 16; ++r) {
+            const int m = mb + 8 * (r / 4) + out_m + r % 4;
+            if (m < M)
+                C[(int64_t)m * N + n] = shift4 ? (blk[r] >> 4) : blk[r];
+        }
+    };
+    auto store_partials = [&](int m0, int n0, int g) __attribute__((always_inline)) {
+        int32_t *P = static_cast<int32_t *>(args.out) + (int64_t)g * M * N;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v4f swv = *reinterpret_cast<const v4f *>(
-                    &SWS(B)[g * BN + wn * TN + j * 32 + q * 8 + out_n]);
+            for (int i = 0; i < FM; ++i)   // int4: exact, the sums are 16 * P
+                store_block_i32(P, acc[j][i], m0 + wm * TM + i * 32, n0 + wn * TN + j * 32, T::int4);
+    };
+
+    auto fold_group = [&](int buf, int g) __attribute__((always_inline)) {
+        float swv[FN];
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j)
+            swv[j] = sws[buf * SWL + g * BN + wn * TN + j * 32 + out_n];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v4f sav = {1.0f, 1.0f, 1.0f, 1.0f};
+                if constexpr (T::fold_sa)
+                    sav = *reinterpret_cast<const v4f *>(
+                        &sas[buf * SAL + g * BM + wm * TM + i * 32 + q * 8 + out_m]);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float sc = T::fold_sa ? sav[i] * swv[r] : swv[r];
+                        const float sc = T::fold_sa ? sav[r] * swv[j] : swv[j];
                         accf[j][i][4 * q + r] =
                             fmaf((float)acc[j][i][4 * q + r], sc, accf[j][i][4 * q + r]);
                     }
             }
     };
 
-    // After k-step t of stage s: close a group if one ends here.
-    auto after_step = [&](auto B, int s, int t) __attribute__((always_inline)) {
-        if constexpr (T::pergroup) {
-            const int ks = s * 4 + t;
-            if ((t + 1) % SPG == 0 || ks + 1 == nks) {
-                const int gl = t / SPG;                   // group slot within the stage
-                if constexpr (T::partials)
-                    store_partials(s * NG + gl);
-                else
-                    fold_group(B, gl);
+    // ---- the tile's outputs from the final sums
+    auto epilogue = [&](int m0, int n0) __attribute__((always_inline)) {
+        if constexpr (MODE == GemmMode::I32) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    store_block_i32(static_cast<int32_t *>(args.out), acc[j][i],
+                                    m0 + wm * TM + i * 32, n0 + wn * TN + j * 32, false);
+        } else if constexpr (!T::partials) {
+            uint16_t *Y = static_cast<uint16_t *>(args.out);
+            // whole tile inside the output and rows of an even length: every
+            // pair store is in bounds and 4-byte aligned
+            const bool fast = m0 + BM <= M && n0 + BN <= N && (N & 1) == 0;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int mb = m0 + wm * TM + i * 32;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // per-token scales of rows mb + 8q + out_m + 0..3
+                    v4f sav = {1.0f, 1.0f, 1.0f, 1.0f};
+                    if constexpr (MODE != GemmMode::PG)
+                        sav = *reinterpret_cast<const v4f *>(&eps[wm * TM + i * 32 + q * 8 + out_m]);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int n = n0 + wn * TN + j * 32 + out_n;
+                        float v[4];
+                        if constexpr (MODE == GemmMode::PC) {
+                            // sw[n] (clamped at N - 1 by the scale copies)
+                            const float swn = eps[BM + wn * TN + j * 32 + out_n];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                v[r] = rescale_pc(acc[j][i][4 * q + r], sav[r], swn);
+                        } else if constexpr (MODE == GemmMode::PG) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                v[r] = accf[j][i][4 * q + r];
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)   // W4: per-token scale, undo x16 (exact)
+                                v[r] = accf[j][i][4 * q + r] * (sav[r] * 0.0625f);
+                        }
+                        const int m = mb + q * 8 + out_m;   // rows m .. m+3
+                        if (fast) {
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {    // rows m+2h, m+2h+1
+                                const uint32_t w = pair_rows_to_cols(pack_h2(v[2 * h], v[2 * h + 1]),
+                                                                     pair_sel);
+                                const int mr = m + 2 * h + (lane & 1);
+                                const int nc = n - (lane & 1);
+                                *reinterpret_cast<uint32_t *>(Y + (int64_t)mr * N + nc) = w;
+                            }
+                        } else if (n < N) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (m + r < M)
+                                    Y[(int64_t)(m + r) * N + n] = f2h(v[r]);
+                        }
+                    }
+                    // a quarter of the sums at a time: keeps the reads of
+                    // the others from being hoisted here
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     };
 
-    // ---- pipeline.  Stage t lives in LDS buffer t % 3.  Its copies are
-    // issued during step 3 of iteration t-3 (int4 weights: loaded into
-    // registers in iteration t-2 and unpacked to LDS before the barrier of
-    // iteration t-1).  Iteration s: steps 0-2 from buffer s%3; wait for
-    // stage s+1's copies and barrier; issue stage s+3's copies into buffer
-    // s%3 (nobody reads it any more); step 3, which also reads the first
-    // fragments of stage s+1.  Every iteration issues the same memory
-    // operations -- past the last stage the copies repeat the last stage
-    // into a buffer nobody reads -- so the loop has no branches around them
-    // and every wait count is a constant.
-    const int last = nstage - 1;
+    // ---- pipeline.  Stage u of the stream lives in LDS buffer u % 3.  Its
+    // copies are issued in four parts: part A during step 3 of iteration u-3,
+    // right after the barrier that frees the buffer, and parts 0-2 during
+    // steps 0-2 of iteration u-2 (int4 weights: loaded into registers in
+    // iteration u-2 and unpacked to LDS before the barrier of iteration u-1).
+    // Iteration u: steps 0-2 from buffer u%3; wait for stage u+1 and barrier;
+    // step 3, which also reads the first fragments of stage u+1; after the
+    // last stage of a tile, its epilogue.  Every iteration issues the same
+    // copies -- past the end of the stream they repeat the last stage into a
+    // buffer nobody reads -- so every wait count is a constant.
     auto main_loop = [&](auto KFULL) __attribute__((always_inline)) {
         constexpr bool kfull = decltype(KFULL)::value;   // K % 128 == 0: every k-step exists
-        dma_stage(std::integral_constant<int, 0>(), 0);
+        Src cp;                                       // stage 0, then 1, 2 (prologue)
+        cp.v = 0; cp.s = 0; cp.buf = 0;
+        set_tile(cp, 0);
+        int cm0 = cp.m0, cn0 = cp.n0, ctile = 0;      // the tile being computed
+        if constexpr (EW > 0)
+            issue_epilogue_scales(cm0, cn0);          // complete before stage 0 does
+        issue_copies(cp, 0, NCW);
         if constexpr (T::int4) {
-            w4_load(0);
-            w4_store(std::integral_constant<int, 0>());
-            w4_load(min(1, last));
+            w4_load(cp);
+            w4_store(0);
         }
-        dma_stage(std::integral_constant<int, 1>(), min(1, last));
-        dma_stage(std::integral_constant<int, 2>(), min(2, last));
-        wait_vmcnt<2 * ND>();
+        advance(cp);
+        if constexpr (T::int4)
+            w4_load(cp);
+        issue_copies(cp, 0, NCW);
+        advance(cp);
+        issue_copies(cp, 0, CA);
+        Src c2 = cp;                                  // stage u+2: parts 0-2 in iteration u
+        advance(cp);
+        Src c3 = cp;                                  // stage u+3: part A in iteration u
+        wait_vmcnt<ND + CA>();
         lds_barrier();
-        read_frag(f0, std::integral_constant<int, 0>(), 0);
+        read_frag(f0, 0, 0);
 
-        auto iteration = [&](auto B, int s) __attribute__((always_inline)) {
-            constexpr int b = decltype(B)::value;
-            constexpr int b1 = (b + 1) % 3;
+        int b = 0, s = 0;                             // buffer and in-tile stage of iteration u
+        for (int u = 0; u < U; ++u) {
+            const int b1 = b == 2 ? 0 : b + 1;
             const int ks0 = s * 4;
-            auto step = [&](auto TC) __attribute__((always_inline)) {
+            auto step = [&](auto TC, const Src &src, int c0, int n) __attribute__((always_inline)) {
                 constexpr int t = decltype(TC)::value;
                 Frag &cur = (t & 1) ? f1 : f0;
                 Frag &nxt = (t & 1) ? f0 : f1;
                 if (kfull || ks0 + t < nks) {
-                    if constexpr (t < 3) {
-                        if (kfull || ks0 + t + 1 < nks)
-                            read_frag(nxt, B, t + 1);
+                    // the next step's fragments: of this stage, or (step 3)
+                    // of the next stage (which nothing overwrites before it
+                    // is computed, also across a tile's epilogue)
+                    const bool reads = t < 3 ? (kfull || ks0 + t + 1 < nks) : true;
+                    const int rbuf = t < 3 ? b : b1, rt = (t + 1) & 3;
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (T::pergroup) {
+                        if constexpr (t % SPG == 0)
+                            mfma_step(cur, std::true_type(), nxt, reads, rbuf, rt, src, c0, n);
+                        else
+                            mfma_step(cur, std::false_type(), nxt, reads, rbuf, rt, src, c0, n);
+                    } else if constexpr (t == 0) {
+                        if (s == 0)                   // a tile's first k-step
+                            mfma_step(cur, std::true_type(), nxt, reads, rbuf, rt, src, c0, n);
+                        else
+                            mfma_step(cur, std::false_type(), nxt, reads, rbuf, rt, src, c0, n);
                     } else {
-                        read_frag(nxt, std::integral_constant<int, b1>(), 0);
+                        mfma_step(cur, std::false_type(), nxt, reads, rbuf, rt, src, c0, n);
                     }
-                    // keep the reads for the next step ahead of this step's
-                    // MFMAs, which use fragments read one step earlier
                     __builtin_amdgcn_sched_barrier(0);
-                    mfma_step(cur, T::pergroup && (t % SPG == 0));
-                    __builtin_amdgcn_sched_barrier(0);
-                    after_step(B, s, t);
+                    if constexpr (T::pergroup) {      // close a group if one ends here
+                        const int ks = ks0 + t;
+                        if ((t + 1) % SPG == 0 || ks + 1 == nks) {
+                            const int gl = t / SPG;   // group slot within the stage
+                            if constexpr (T::partials)
+                                store_partials(cm0, cn0, s * NG + gl);
+                            else
+                                fold_group(b, gl);
+                        }
+                    }
+                } else {
+                    // a K % 128 == 64 tail: the step does not exist, its copies
+                    // (and after the barrier the next stage's fragments) do
+                    if constexpr (t == 3)
+                        read_frag(nxt, b1, 0);
+                    issue_copies(src, c0, n);
                 }
             };
-            step(std::integral_constant<int, 0>());
-            step(std::integral_constant<int, 1>());
-            step(std::integral_constant<int, 2>());
-            // stage s+1 complete and visible; buffer b free
+            step(std::integral_constant<int, 0>(), c2, CA, C0);
+            step(std::integral_constant<int, 1>(), c2, CA + C0, C1);
+            step(std::integral_constant<int, 2>(), c2, CA + C0 + C1, C2);
+            // stage u+1 complete and visible; buffer b free
             if constexpr (T::int4)
-                w4_store(std::integral_constant<int, b1>());
+                w4_store(b1);
             wait_vmcnt<ND>();
             lds_barrier();
             if constexpr (T::int4)
-                w4_load(min(s + 2, last));
-            if constexpr (T::fold_sw) {
-                // the fold after step 3 still reads this stage's scales from
-                // buffer b: copy into it only afterwards
-                step(std::integral_constant<int, 3>());
-                dma_stage(B, min(s + 3, last));
+                w4_load(c2);
+            step(std::integral_constant<int, 3>(), c3, 0, CA);
+
+            if (s + 1 == nstage) {                    // the tile is done
+                if constexpr (EW > 0) {
+                    if (nstage < 3) {                 // its scales may still be in flight
+                        wait_vmcnt<0>();
+                        lds_barrier();
+                    }
+                }
+                epilogue(cm0, cn0);
+                clear_accf();
+                s = 0;
+                if (++ctile < ntile) {
+                    tile_origin(ctile, cm0, cn0);
+                    if constexpr (EW > 0) {
+                        lds_barrier();                // every wave is done with the scales
+                        issue_epilogue_scales(cm0, cn0);
+                    }
+                }
             } else {
-                dma_stage(B, min(s + 3, last));
-                step(std::integral_constant<int, 3>());
+                ++s;
             }
-        };
-        for (int s = 0; s < nstage; s += 3) {
-            iteration(std::integral_constant<int, 0>(), s);
-            if (s + 1 < nstage) {
-                iteration(std::integral_constant<int, 1>(), s + 1);
-                if (s + 2 < nstage)
-                    iteration(std::integral_constant<int, 2>(), s + 2);
-            }
+            c2 = c3;
+            advance(c3);
+            b = b1;
         }
         // no copy may still be writing LDS when the workgroup ends
         wait_vmcnt<0>();
@@ -502,85 +720,20 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         main_loop(std::true_type());
     else
         main_loop(std::false_type());
+}
 
-    // ---- epilogue
-    if constexpr (T::partials) {
-        return;
-    } else if constexpr (MODE == GemmMode::I32) {
-        int32_t *C = static_cast<int32_t *>(args.out);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int m = m0 + wm * TM + i * 32 + out_m;
-            if (m >= M)
-                continue;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + wn * TN + j * 32 + q * 8 + out_n;
-                    const v4i v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
-                                   acc[j][i][4 * q + 3]};
-                    int32_t *dst = C + (int64_t)m * N + n;
-                    if (n + 3 < N && (N & 3) == 0) {
-                        *reinterpret_cast<v4i *>(dst) = v;
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (n + r < N)
-                                dst[r] = v[r];
-                    }
-                }
-        }
-    } else {
-        uint16_t *Y = static_cast<uint16_t *>(args.out);
-        const bool vec_ok = (N & 3) == 0;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int m = m0 + wm * TM + i * 32 + out_m;
-            if (m >= M)
-                continue;
-            const float sa = (MODE == GemmMode::PG) ? 1.0f : args.sa[m];
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + wn * TN + j * 32 + q * 8 + out_n;
-                    float v[4];
-                    if constexpr (MODE == GemmMode::PC) {
-                        float swq[4];
-                        if (vec_ok && n + 3 < N) {
-                            const float4 t4 = *reinterpret_cast<const float4 *>(args.sw + n);
-                            swq[0] = t4.x; swq[1] = t4.y; swq[2] = t4.z; swq[3] = t4.w;
-                        } else {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                swq[r] = args.sw[min(n + r, N - 1)];
-                        }
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            v[r] = rescale_pc(acc[j][i][4 * q + r], sa, swq[r]);
-                    } else if constexpr (MODE == GemmMode::PG) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            v[r] = accf[j][i][4 * q + r];
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            v[r] = accf[j][i][4 * q + r] * (sa * 0.0625f);   // W4: per-token scale, undo x16 (exact)
-                    }
-                    uint16_t *dst = Y + (int64_t)m * N + n;
-                    if (vec_ok && n + 3 < N) {
-                        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_h2(v[0], v[1]),
-                                                                     pack_h2(v[2], v[3]));
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (n + r < N)
-                                dst[r] = f2h(v[r]);
-                    }
-                }
-        }
-    }
+// Workgroups of one instantiation that fit on a compute unit at once.
+template <int BM, int BN, int WM, int WN, GemmMode MODE, int GS>
+int groups_per_cu()
+{
+    static const int occ = [] {
+        int o = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, gemm_kernel<BM, BN, WM, WN, MODE, GS>,
+                                                         WM * WN * 64, 0) != hipSuccess || o < 1)
+            o = 1;
+        return o;
+    }();
+    return occ;
 }
 
 template <int BM, int BN, int WM, int WN, GemmMode MODE, int GS>
@@ -588,8 +741,10 @@ void launch_cfg(const GemmArgs &a, hipStream_t st)
 {
     const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     const int group_m = 4;
-    const unsigned nb = (unsigned)tiles_m * (unsigned)tiles_n;
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, MODE, GS>), dim3(nb), dim3(WM * WN * 64), 0, st,
+    const int64_t tiles = (int64_t)tiles_m * tiles_n;
+    const int64_t resident = (int64_t)a.num_cu * groups_per_cu<BM, BN, WM, WN, MODE, GS>();
+    const unsigned grid = (unsigned)(tiles < resident ? tiles : resident);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, MODE, GS>), dim3(grid), dim3(WM * WN * 64), 0, st,
                        a, tiles_m, tiles_n, group_m);
 }
 

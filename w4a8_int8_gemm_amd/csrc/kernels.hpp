@@ -32,6 +32,7 @@ struct GemmArgs {
     const float *sw;      // [N] or [N, G]
     void *out;            // fp16 [M, N] or int32 [M, N] / [G, M, N]
     int M, N, K, gs;
+    int num_cu;           // compute units of the device (sizes the persistent grid)
 };
 
 void launch_gemm(GemmMode mode, const GemmArgs &a, hipStream_t st);
