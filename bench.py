@@ -7,9 +7,11 @@ linear() makes for M > 1 -- at M=4096, N=10240, K=2560 with outlier-laden
 synthetic activations.  Inputs are resident in HBM before timing starts; the
 offline weight quantization is done once, outside the timed region.
 
-Prints one JSON line:  value = 2*M*N*K / step time (TOPS, act-quant included),
-roofline = the GEMM kernel's own rate against the dense int8 MFMA peak (from
-HIP events around each GEMM launch in the timed loop), cpu_baseline = the CPU
+Prints one JSON line:  value = 2*M*N*K / step time (TOPS, act-quant included;
+wall clock over K steps with a device synchronization on both sides),
+roofline = the GEMM kernel's own rate against the dense int8 MFMA peak (its
+average launch duration from HIP events around K back-to-back launches on the
+stream the steps use, right after the timed steps), cpu_baseline = the CPU
 oracle timed on a bounded sample of rows of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -18,6 +20,7 @@ oracle timed on a bounded sample of rows of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -148,30 +151,56 @@ def main():
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
-        w.quantize_act(xd, 0, out=xq, scale=xs)
-        w.w8a8_gemm_pc(xq, xs, wq, sw, out=y)
+    # The timed loop calls the C entry points directly with the pointers
+    # marshalled once: the per-call checks of the torch wrappers cost more
+    # host time than a step takes on the GPU, which would leave the GPU idle
+    # between launches and time the host instead.
+    L = w.lib()
+    P = ctypes.c_void_p
+    xp, xqp, xsp, wqp, swp, yp = (P(t.data_ptr()) for t in (xd, xq, xs, wq, sw, y))
+    sp = P(stream.cuda_stream)
 
+    def quant():
+        w.check(L.quantize_act(xp, M, K, 0, xqp, xsp, sp))
+
+    def gemm():
+        w.check(L.w8a8_gemm_pc(xqp, xsp, wqp, swp, yp, M, N, K, sp))
+
+    # same results as the checked wrappers
+    w.quantize_act(xd, 0, out=xq, scale=xs)
+    w.w8a8_gemm_pc(xq, xs, wq, sw, out=y)
+    y_ref = y.clone()
     for _ in range(args.warmup):
-        step()
+        quant()
+        gemm()
     torch.cuda.synchronize()
+    assert torch.equal(y, y_ref), "raw entry points disagree with the wrappers"
 
     K_steps = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K_steps):
-        ev[i][0].record(stream)
-        w.quantize_act(xd, 0, out=xq, scale=xs)
-        ev[i][1].record(stream)
-        w.w8a8_gemm_pc(xq, xs, wq, sw, out=y)
-        ev[i][2].record(stream)
+    e_start.record(stream)
+    for _ in range(K_steps):
+        quant()
+        gemm()
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_step_us = e_start.elapsed_time(e_end) * 1e3 / K_steps
 
-    q_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K_steps)])
-    g_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K_steps)])
-    ms_per_step = wall * 1e3 / K_steps
+    # Per-kernel launch durations: each kernel K times back to back on the
+    # same stream, one event pair around the batch (an event record between
+    # two kernels costs a few microseconds of its own on this stack).
+    def batch_us(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K_steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K_steps
+    gemm_us, quant_us = batch_us(gemm), batch_us(quant)
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
 
@@ -182,15 +211,16 @@ def main():
     w.linear(w.Mode.W8A8_PC, xd, wq, sw, workspace=ws, out=y_lin)
     torch.cuda.synchronize()
     same = bool(torch.equal(y_lin, y))
+    ylp, wsp = P(y_lin.data_ptr()), P(ws.data_ptr())
     t1 = time.perf_counter()
     for _ in range(K_steps):
-        w.linear(w.Mode.W8A8_PC, xd, wq, sw, workspace=ws, out=y_lin)
+        w.check(L.linear(int(w.Mode.W8A8_PC), xp, M, K, wqp, swp, 0, N, ylp, wsp, ws.numel(), sp))
     torch.cuda.synchronize()
     linear_ms = (time.perf_counter() - t1) * 1e3 / K_steps
 
-    gemm_ms = float(g_ms.mean())
+    gemm_ms = gemm_us * 1e-3
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    quant_ms = float(q_ms.mean())
+    quant_ms = quant_us * 1e-3
     quant_bytes = M * K * 2 + M * K + M * 4            # read fp16 x, write int8 codes + scales
     gemm_bytes_alg = M * K + N * K + M * N * 2 + (M + N) * 4
     traffic = traffic_from_profiles(gemm_bytes_alg)
@@ -224,6 +254,7 @@ def main():
                          "achieved_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
                          "peak_GBps": PEAK_HBM_GBS,
                          "frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "gpu_us_per_step": round(gpu_step_us, 2),
         "linear_ms_per_step": round(linear_ms, 5),
         "linear_matches_kernels": same,
     }

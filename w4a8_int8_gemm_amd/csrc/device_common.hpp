@@ -49,23 +49,46 @@ __device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d)
            ((uint32_t)d << 24);
 }
 
-// Butterfly max over groups of `width` consecutive lanes (width a power of two <= 64).
+// Reductions over groups of `width` consecutive lanes (2, 4, 8, 16 or 64)
+// with DPP lane moves.  Within a row of 16 lanes: swap neighbours, then
+// pairs (quad permutes), then mirror half rows and rows -- after each move
+// every lane of a group holds the group's value, and its partner lies in the
+// sibling group.  Across the four rows of a wave: row broadcasts carry row 0
+// into row 1 and row 2 into row 3, then the lower half into the upper; lane
+// 63 ends with the total, which is read into every lane.  Lanes that a move
+// does not reach take 0, the identity of both max (of unsigned values) and +.
+#define W4A8_DPP(x, ctrl, rows) __builtin_amdgcn_update_dpp(0, (x), (ctrl), (rows), 0xf, false)
+
+template <int width, typename T, typename Op>
+__device__ __forceinline__ T lane_reduce(T v, Op op)
+{
+    static_assert(width == 2 || width == 4 || width == 8 || width == 16 || width == 64,
+                  "reduction width");
+    v = op(v, (T)W4A8_DPP((int)v, 0xb1, 0xf));          // quad_perm [1,0,3,2]
+    if constexpr (width >= 4)
+        v = op(v, (T)W4A8_DPP((int)v, 0x4e, 0xf));      // quad_perm [2,3,0,1]
+    if constexpr (width >= 8)
+        v = op(v, (T)W4A8_DPP((int)v, 0x141, 0xf));     // row_half_mirror
+    if constexpr (width >= 16)
+        v = op(v, (T)W4A8_DPP((int)v, 0x140, 0xf));     // row_mirror
+    if constexpr (width == 64) {
+        v = op(v, (T)W4A8_DPP((int)v, 0x142, 0xa));     // row_bcast:15 into rows 1, 3
+        v = op(v, (T)W4A8_DPP((int)v, 0x143, 0xc));     // row_bcast:31 into rows 2, 3
+        v = (T)__builtin_amdgcn_readlane((int)v, 63);
+    }
+    return v;
+}
+
 template <int width>
 __device__ __forceinline__ uint32_t group_max_u32(uint32_t v)
 {
-#pragma unroll
-    for (int off = 1; off < width; off <<= 1)
-        v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-    return v;
+    return lane_reduce<width>(v, [](uint32_t a, uint32_t b) { return max(a, b); });
 }
 
 template <int width>
 __device__ __forceinline__ int group_sum_i32(int v)
 {
-#pragma unroll
-    for (int off = 1; off < width; off <<= 1)
-        v += __shfl_xor(v, off, 64);
-    return v;
+    return lane_reduce<width>(v, [](int a, int b) { return a + b; });
 }
 
 // max(|h|) of the eight fp16 values in a 16-byte chunk, as fp16 bits.  For
@@ -81,26 +104,32 @@ __device__ __forceinline__ uint32_t absmax_bits8(uint4 v)
 }
 
 // Quantize the eight fp16 values of a chunk with scale s (r = fl32(1/s)).
-// Fast path for all eight; any guarded element sends the whole chunk through
-// the division rule.  Returns the eight codes as two dwords.
+// Fast path for all eight; if any of them is guarded, the whole chunk goes
+// through the division rule.  Returns the eight codes as two dwords.
 __device__ __forceinline__ uint2 quant_chunk8(uint4 v, float s, float r, float qmax)
 {
     if (s == 0.0f)
         return make_uint2(0u, 0u);
-    float x0 = lo_h2f(v.x), x1 = hi_h2f(v.x), x2 = lo_h2f(v.y), x3 = hi_h2f(v.y);
-    float x4 = lo_h2f(v.z), x5 = hi_h2f(v.z), x6 = lo_h2f(v.w), x7 = hi_h2f(v.w);
-    bool slow = false;
-    int q0 = quant_code_fast(x0, r, qmax, slow), q1 = quant_code_fast(x1, r, qmax, slow);
-    int q2 = quant_code_fast(x2, r, qmax, slow), q3 = quant_code_fast(x3, r, qmax, slow);
-    int q4 = quant_code_fast(x4, r, qmax, slow), q5 = quant_code_fast(x5, r, qmax, slow);
-    int q6 = quant_code_fast(x6, r, qmax, slow), q7 = quant_code_fast(x7, r, qmax, slow);
-    if (__builtin_expect(slow, 0)) {
-        q0 = quant_code_div(x0, s, qmax); q1 = quant_code_div(x1, s, qmax);
-        q2 = quant_code_div(x2, s, qmax); q3 = quant_code_div(x3, s, qmax);
-        q4 = quant_code_div(x4, s, qmax); q5 = quant_code_div(x5, s, qmax);
-        q6 = quant_code_div(x6, s, qmax); q7 = quant_code_div(x7, s, qmax);
+    float x[8] = {lo_h2f(v.x), hi_h2f(v.x), lo_h2f(v.y), hi_h2f(v.y),
+                  lo_h2f(v.z), hi_h2f(v.z), lo_h2f(v.w), hi_h2f(v.w)};
+    float t[8];
+    float far = 0.0f;                 // largest distance to an integer
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        t[i] = quant_fast_t(x[i], r);
+        far = fmaxf(far, quant_fast_resid(t[i]));
     }
-    return make_uint2(pack_i8x4(q0, q1, q2, q3), pack_i8x4(q4, q5, q6, q7));
+    int q[8];
+    if (__builtin_expect(quant_fast_slow(far), 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            q[i] = quant_code_div(x[i], s, qmax);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            q[i] = quant_fast_code(t[i]);
+    }
+    return make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]));
 }
 
 // Per-channel rescale of one int32 sum; the same operation order everywhere

@@ -9,13 +9,17 @@
 //
 // Two ways to reach the same code:
 //  * quant_code_div: the rule as written (one IEEE division per element);
-//  * quant_code_fast: one fma with r = fl32(1/s) plus a guard.  The fma
-//    result v = fl32(|x| r + 1/2) differs from |fl32(x/s)| + 1/2 by less than
-//    2^-15 whenever |x/s| <= 128 (r carries one rounding, the fma one more,
-//    the division one), so floor(v) equals round_half_away(fl32(x/s)) unless
-//    v lies within 2^-15 of an integer.  The guard flags every v within 2^-14
-//    of an integer; those elements must be recomputed with quant_code_div.
-//
+//  * quant_code_fast: t = fl32(x r) with r = fl32(1/s), code rint(t), plus a
+//    guard.  t differs from x/s by at most |x/s| 2^-23 (r and the product
+//    carry one rounding each), which is below 1.6e-5 for |x/s| <= 128, so
+//    rint(t) equals round_half_away(fl32(x/s)) unless x/s lies within that
+//    distance of a half-integer.  The guard flags every t whose distance to
+//    its nearest integer exceeds 1/2 - 2^-14 (exact ties included, where rint
+//    and round_half_away differ); those elements take quant_code_div.  The
+//    clamp is never active on this path: with |x| <= amax (s is derived from
+//    the slice's own amax), |t| <= qmax (1 + 2^-22) < qmax + 1/2 - 2^-14.
+//    The test is split so a kernel can take the maximum distance over
+//    several elements and compare once.
 // This header is also compiled for the host by the CPU test suite, which
 // checks the fast path plus guard against the division rule on every fp16
 // input for many scales.
@@ -47,16 +51,20 @@ W4A8_HD int quant_code_div(float x, float s, float qmax)
 // Guard width: v within this distance of an integer goes to the slow path.
 #define W4A8_QUANT_GUARD 0x1p-14f
 
-// Fast path.  `r` is fl32(1/s) for s != 0.  Sets `slow` (never clears it)
-// when the element must be recomputed with quant_code_div.
+// Fast path, in parts: the scaled value, its distance to the nearest
+// integer, the code, and whether a distance needs the division rule.
+W4A8_HD float quant_fast_t(float x, float r) { return fmaf(x, r, -0.0f); }   // == x * r
+W4A8_HD float quant_fast_resid(float t) { return fabsf(t - rintf(t)); }      // exact
+W4A8_HD int quant_fast_code(float t) { return (int)rintf(t); }
+W4A8_HD bool quant_fast_slow(float resid) { return resid > 0.5f - W4A8_QUANT_GUARD; }
+
+// One element: code and guard (|x| <= amax of the slice, see above).
 W4A8_HD int quant_code_fast(float x, float r, float qmax, bool &slow)
 {
-    float v = fmaf(fabsf(x), r, 0.5f);
-    float f = floorf(v);
-    float d = v - f;                           // exact: v and f share a binade
-    slow |= fabsf(d - 0.5f) > 0.5f - W4A8_QUANT_GUARD;
-    f = fminf(f, qmax);
-    return (int)copysignf(f, x);
+    (void)qmax;
+    const float t = quant_fast_t(x, r);
+    slow |= quant_fast_slow(quant_fast_resid(t));
+    return quant_fast_code(t);
 }
 
 }  // namespace w4a8
