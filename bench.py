@@ -16,6 +16,7 @@ oracle timed on a bounded sample of rows of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --copy-probe      # plain copy kernel, for HBM counter scaling
+    python bench.py --suite [--steps K]   # timing table over every workload shape
 """
 from __future__ import annotations
 
@@ -53,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
+    ap.add_argument("--suite", action="store_true",
+                    help="time every workload shape (a table, not the JSON line)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain copy of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -85,6 +88,93 @@ def copy_probe():
         b.copy_(a)
     torch.cuda.synchronize()
     log(f"copy probe: 5 copies of {n} bytes")
+
+
+def suite(reps):
+    """Per-workload kernel timings (not the JSON line): every shape of
+    synth.WORKLOADS through its path, each kernel `reps` times back to back
+    between two events, through the C entry points.  The decode shape (M=1)
+    is timed warm (weights resident in the 256 MB Infinity Cache after the
+    first call) and cold (a 1 GiB buffer written between calls; run under
+    `rocprofv3 --kernel-trace` for those per-dispatch durations)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a8_int8_gemm_amd as w
+
+    torch.cuda.set_device(0)
+    L = w.lib()
+    P = ctypes.c_void_p
+    st = torch.cuda.current_stream()
+    sp = P(st.cuda_stream)
+
+    def ptr(t):
+        return P(t.data_ptr())
+
+    def b2b(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    rows = []
+    for name, wl in synth.WORKLOADS.items():
+        mode, gs = wl["mode"], wl["gs"]
+        for (M, N, K) in wl["shapes"]:
+            x = torch.from_numpy(synth.activations(M, K, seed=1, outliers=wl["outliers"])).cuda()
+            wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
+            y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            ops = 2.0 * M * N * K
+            act_gs = gs if mode == "pg" else 0
+            if mode == "w4a8":
+                wq, sw = w.pack_weight_int4(wt, gs)
+            else:
+                wq, sw = w.quantize_weight_int8(wt, gs if mode == "pg" else 0)
+            del wt
+            xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+            xs = torch.empty((M, K // act_gs if act_gs else 1), dtype=torch.float32,
+                             device="cuda")
+            if mode == "pc" and M == 1:
+                fn = lambda: w.check(L.int8_mv(ptr(x), ptr(wq), ptr(sw), ptr(y), N, K, None,
+                                               None, sp))
+                us = b2b(fn)
+                flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+                for _ in range(reps):
+                    flush.fill_(1)
+                    fn()
+                torch.cuda.synchronize()
+                del flush
+                wbytes = N * K + 2 * K + 6 * N
+                rows.append(f"{name:10s} M={M:5d} N={N:5d} K={K:5d}  int8_mv {us:8.2f} us warm  "
+                            f"{wbytes / us / 1e3:7.0f} GB/s ({100 * wbytes / us / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak)")
+                continue
+            q = lambda: w.check(L.quantize_act(ptr(x), M, K, act_gs, ptr(xq), ptr(xs), sp))
+            if mode == "pc":
+                g = lambda: w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y),
+                                                   M, N, K, sp))
+            elif mode == "pg":
+                g = lambda: w.check(L.w8a8_gemm_pg(ptr(xq), ptr(xs), ptr(wq), ptr(sw), gs, ptr(y),
+                                                   M, N, K, sp))
+            else:
+                g = lambda: w.check(L.w4a8_gemm(ptr(xq), ptr(xs), ptr(wq), ptr(sw), gs, ptr(y),
+                                                M, N, K, sp))
+            q()
+            qus, gus = b2b(q), b2b(g)
+            qbytes = 3 * M * K
+            rows.append(f"{name:10s} M={M:5d} N={N:5d} K={K:5d}  quantize {qus:7.2f} us "
+                        f"({qbytes / qus / 1e3:5.0f} GB/s) | gemm {gus:8.2f} us "
+                        f"{ops / gus / 1e6:7.1f} TOPS ({100 * ops / gus / 1e6 / PEAK_INT8_TOPS:4.1f}% "
+                        f"of int8 peak) | step {ops / (qus + gus) / 1e6:7.1f} TOPS")
+            print(rows[-1], flush=True)
+            del x, y, wq, sw, xq, xs
+            torch.cuda.empty_cache()
+    print("\n".join(rows), flush=True)
 
 
 def cpu_baseline(x, wt_q, sw, M, N, K, target_s):
@@ -131,6 +221,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.suite:
+        suite(args.steps)
         return
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"

@@ -9,28 +9,31 @@
 // unpacked to INT8 before the INT8 matmul ("cider" post, modes table).
 //
 // Design (CDNA4, wave64, one wave per SIMD for the large tiles):
-//  * One workgroup computes a BM x BN tile of Y (m x n) with WM x WN waves.
+//  * One workgroup computes BM x BN tiles of Y (m x n) with WM x WN waves.
 //    Both operands are K-contiguous.  v_mfma_i32_32x32x32_i8 takes the
-//    weight fragment as its A operand (32 n-rows x 32 k, 16 bytes per lane)
-//    and the activation fragment as B, so each lane's int32 results come in
-//    runs of four consecutive n of one output row (8-byte fp16 stores).  This
-//    MFMA sustains close to the int8 peak with a single wave per SIMD, which
-//    the large per-wave tiles need (they keep LDS traffic per op low).
-//  * K advances in stages of 128 bytes through three LDS buffers.  Global
-//    loads for stages s+2 and s+3 are in flight in two register sets while
-//    stage s is computed; stage s+2 is written to LDS at the end of stage s,
-//    so stage s+1 is already resident when stage s ends and its first
-//    fragments are read while the last MFMAs of stage s run.  Within a stage
-//    the fragments of k-step t+1 are read while the MFMAs of step t run.
-//  * 16-byte chunks are XOR-swizzled per LDS row.
+//    activation fragment (32 m-rows x 32 k, 16 bytes per lane) as its A
+//    operand and the weight fragment as B, so each lane holds one output
+//    column n and runs of four rows.  This MFMA sustains close to the int8
+//    peak with a single wave per SIMD, which the large per-wave tiles need
+//    (they keep LDS reads per MFMA low).
+//  * K advances in stages of 128 bytes through a ring of three LDS buffers.
+//    Stages are copied from global memory straight into LDS (buffer loads
+//    with the lds modifier, 16-byte chunks XOR-swizzled per row); the copies
+//    of one stage are spread over four k-steps between the MFMAs, and the
+//    only waits are explicit vmcnt counts before an LDS-only barrier.
+//  * Per-tile buffer resources make rows past the end of X or W read as
+//    zeros, so copies need no per-lane clamping.
+//  * The kernel is persistent: each workgroup walks a list of tiles and its
+//    stages form one stream across them, so the next tile's first stages are
+//    in flight while the current one finishes.
 //  * int4 weights are loaded packed (half the bytes), unpacked in registers to
 //    16 * code (the nibble placed in the high half of each byte, which is
 //    the code times 16 as a signed byte) and stored to LDS in the same int8
-//    layout; the factor 16 is folded into the weight scales (exact).
+//    layout; the factor 16 is undone in the epilogue (exact).
 //  * Per-group modes restart the int32 accumulators for every group and fold
 //    them into fp32 accumulators with the group's scales, which are staged
 //    through LDS together with the tiles.
-//  * Workgroups are remapped so that each XCD (one L2 each) works on a
+//  * Workgroups are renumbered so that each XCD (one L2 each) works on a
 //    contiguous range of tiles, ordered in groups of `group_m` tile rows.
 #include <type_traits>
 
