@@ -294,6 +294,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / K_steps
     gemm_us, quant_us = batch_us(gemm), batch_us(quant)
+    ms_per_step = wall * 1e3 / K_steps
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
 

@@ -37,9 +37,14 @@ __device__ __forceinline__ uint16_t f2h(float f)
 __device__ __forceinline__ float lo_h2f(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float hi_h2f(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
 
+// Two fp32 values to two fp16 (a in the low half), each rounded to nearest
+// even as f2h does, in one v_cvt_pk_f16_f32.
 __device__ __forceinline__ uint32_t pack_h2(float a, float b)
 {
-    return (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    asm("" : "+v"(a), "+v"(b));
+    const h2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // Four int codes in [-127, 127] to four bytes, element 0 in the low byte.

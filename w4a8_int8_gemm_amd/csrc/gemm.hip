@@ -48,8 +48,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 128;          // k bytes per LDS stage (four 32-wide MFMA steps)
 
-// Physical 16-byte chunk of logical chunk c (0..7) in LDS row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
+// Physical 16-byte chunk of logical chunk c (0..7) in LDS row r (rows are
+// 128 bytes).  A 16-byte-per-lane LDS read serves 16 lanes per cycle from 64
+// four-byte banks, i.e. two rows' worth; fragment reads put 16 consecutive
+// rows, one logical chunk each, in such a group.  XOR with r & 7 spreads
+// 8 rows over the 8 chunk positions, and the extra flip for rows 8..15 moves
+// them to the other half of the banks' 16-byte slots, so all 16 lanes hit
+// distinct banks (and any 8 consecutive lanes still do).  An involution in
+// c for fixed r.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
 // Unpack 8 int4 codes (one dword, low nibble = even k) into 8 signed bytes
 // holding 16 * code, in natural k order (two dwords).
@@ -98,28 +105,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Direct-to-LDS copies: each lane's bytes from global memory land at
 // M0 + size * lane.  Issued through asm so that the only waits on them are
 // the kernel's own (vmcnt before the barrier that publishes a stage); the
-// "memory" clobber keeps other memory accesses from moving across them.  M0
-// is saved and restored around the copy, and one wait state separates the
-// SALU write of M0 from the load that reads it (a gfx9 hazard).
+// "memory" clobber keeps other memory accesses from moving across them.  One
+// wait state separates the SALU write of M0 from the load that reads it (a
+// gfx9 hazard).  M0 is not restored: nothing else in these kernels uses it
+// (the compiler cannot be told that asm writes M0, so a CPU test checks the
+// kernels' assembly for any other M0 access).
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const lds_void *)p;
 }
-__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds)
-{
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "s"(lds), "v"(src)
-                 : "memory");
-}
 __device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds)
 {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
                  : "s"(lds), "v"(src)
                  : "memory");
 }
@@ -145,14 +143,16 @@ __device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes)
     return r;
 }
 
-// 16 bytes per lane from a buffer resource into LDS at M0 + 16 * lane.
-__device__ __forceinline__ void copy16_buf_to_lds(v4i rsrc, uint32_t voff, uint32_t lds)
+// 16 bytes per lane from a buffer resource into LDS at M0 + 16 * lane, from
+// byte offset voff + soff of the resource.  Lanes whose voff lies past the
+// resource's size read zeros.
+__device__ __forceinline__ void copy16_buf_to_lds(v4i rsrc, uint32_t voff, uint32_t soff,
+                                                  uint32_t lds)
 {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "s"(lds), "v"(voff), "s"(rsrc)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory");
 }
 
@@ -265,11 +265,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     // past the end of the matrix fall outside the tile's buffer resource and
     // read as zeros.
     const int dma_row = lane >> 3;
-    const int dma_chunk = (lane & 7) ^ (dma_row & 7);
     uint32_t vrow[RB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
-        vrow[i] = (uint32_t)(((wave + NW * i) * 8 + dma_row) * K + dma_chunk * 16);
+    for (int i = 0; i < RB; ++i) {
+        const int row = (wave + NW * i) * 8 + dma_row;
+        vrow[i] = (uint32_t)(row * K + swz(row, lane & 7) * 16);
+    }
 
     // Where the copies of one stage come from: the stage's tile, its index
     // within the tile and the LDS buffer it goes to.  Wave-uniform.
@@ -301,15 +302,21 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 
     // Copy c (0 <= c < NCW) of the stage described by `src`.  c is a
     // constant once the callers' loops are unrolled.
-    auto issue_copy = [&](const Src &src, int c) __attribute__((always_inline)) {
+    // The stage's K offset goes in the scalar offset when K % 128 == 0 (every
+    // stage is whole, so a row's bytes never run past its end); for a K tail
+    // it is added to the per-lane offset, which the resource's range check
+    // covers.
+    auto issue_copy = [&](const Src &src, int buf, int c, auto KFULL) __attribute__((always_inline)) {
+        constexpr bool kfull = decltype(KFULL)::value;
         const uint32_t k0 = (uint32_t)(src.s * BK);
+        const uint32_t vk = kfull ? 0u : k0, sk = kfull ? k0 : 0u;
         if (c < XB) {
-            copy16_buf_to_lds(src.rx, vrow[c] + k0,
-                              lds_addr(xs + src.buf * XBUF + (wave + NW * c) * 1024));
+            copy16_buf_to_lds(src.rx, vrow[c] + vk, sk,
+                              lds_addr(xs + buf * XBUF + (wave + NW * c) * 1024));
         } else if (c < XB + WB) {
             const int i = c - XB;
-            copy16_buf_to_lds(src.rw, vrow[i] + k0,
-                              lds_addr(ws + src.buf * WBUF + (wave + NW * i) * 1024));
+            copy16_buf_to_lds(src.rw, vrow[i] + vk, sk,
+                              lds_addr(ws + buf * WBUF + (wave + NW * i) * 1024));
         } else if (c < XB + WB + SAW) {
             if constexpr (T::fold_sa) {
                 const int ins = wave + NW * (c - XB - WB);
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                     const int gi = min(src.s * NG + g, G_ - 1);
                     if (e < NG * BM)
                         copy4_to_lds(args.sa + (int64_t)min(src.m0 + r, M - 1) * G_ + gi,
-                                     lds_addr(sas + src.buf * SAL + ins * 64));
+                                     lds_addr(sas + buf * SAL + ins * 64));
                 }
             }
         } else {
@@ -331,17 +338,18 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                     const int gi = min(src.s * NG + g, G_ - 1);
                     if (e < NG * BN)
                         copy4_to_lds(args.sw + (int64_t)min(src.n0 + r, N - 1) * G_ + gi,
-                                     lds_addr(sws + src.buf * SWL + ins * 64));
+                                     lds_addr(sws + buf * SWL + ins * 64));
                 }
             }
         }
     };
     // Copies [c0, c0 + n) of a stage, back to back.
-    auto issue_copies = [&](const Src &src, int c0, int n) __attribute__((always_inline)) {
+    auto issue_copies = [&](const Src &src, int buf, int c0, int n, auto KFULL)
+                            __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < NCW; ++c)
             if (c >= c0 && c < c0 + n)
-                issue_copy(src, c);
+                issue_copy(src, buf, c, KFULL);
     };
     // The epilogue scales of the tile at (m0, n0); rows and columns past the
     // end repeat the last one.
@@ -457,10 +465,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 
     // The MFMAs of one k-step (restarting the sums when RESTART) on F.
     // Interleaved with them: the fragments of the next step into G (fragment
-    // r after MFMA r * FN * FM / NR, when `reads`), and copies [c0, c0 + n)
-    // of the stage `src` (copy p after MFMA (2p + 1) * FN * FM / (2n)).
+    // r after MFMA r * FN * FM / (2 NR): all within the first half of the
+    // step, so they have landed when the next step starts), and copies
+    // [c0, c0 + n) of the stage `src` (copy p after MFMA (2p + 1) * FN * FM / (2n)).
     auto mfma_step = [&](const Frag &F, auto RESTART, Frag &G, bool reads, int rbuf, int rt,
-                         const Src &src, int c0, int n) __attribute__((always_inline)) {
+                         const Src &src, int sbuf, int c0, int n, auto KFULL)
+                         __attribute__((always_inline)) {
         constexpr bool restart = decltype(RESTART)::value;
         constexpr int NM = FN * FM;
 #pragma unroll
@@ -472,13 +482,13 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
             if (reads) {
 #pragma unroll
                 for (int r = 0; r < NR; ++r)
-                    if ((r * NM) / NR == k)
+                    if ((r * NM) / (2 * NR) == k)
                         read_one(G, rbuf, rt, r);
             }
 #pragma unroll
             for (int p = 0; p < NCW; ++p)
                 if (p < n && k == ((2 * p + 1) * NM) / (2 * n))
-                    issue_copy(src, c0 + p);
+                    issue_copy(src, sbuf, c0 + p, KFULL);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -544,6 +554,16 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
             // whole tile inside the output and rows of an even length: every
             // pair store is in bounds and 4-byte aligned
             const bool fast = m0 + BM <= M && n0 + BN <= N && (N & 1) == 0;
+            // this lane's store position relative to a pair of rows: even
+            // lanes write row m at columns n, n+1; odd lanes row m+1 at n-1, n
+            const uint32_t lane_off =
+                (uint32_t)(((out_m + (lane & 1)) * N + out_n - (lane & 1)) * 2);
+            float swn[FN];
+            if constexpr (MODE == GemmMode::PC) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j)   // sw[n] (clamped at N - 1 by the scale copies)
+                    swn[j] = eps[BM + wn * TN + j * 32 + out_n];
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int mb = m0 + wm * TM + i * 32;
@@ -555,14 +575,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                         sav = *reinterpret_cast<const v4f *>(&eps[wm * TM + i * 32 + q * 8 + out_m]);
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        const int n = n0 + wn * TN + j * 32 + out_n;
+                        const int nb = n0 + wn * TN + j * 32;
                         float v[4];
                         if constexpr (MODE == GemmMode::PC) {
-                            // sw[n] (clamped at N - 1 by the scale copies)
-                            const float swn = eps[BM + wn * TN + j * 32 + out_n];
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
-                                v[r] = rescale_pc(acc[j][i][4 * q + r], sav[r], swn);
+                                v[r] = rescale_pc(acc[j][i][4 * q + r], sav[r], swn[j]);
                         } else if constexpr (MODE == GemmMode::PG) {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
@@ -572,21 +590,24 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                             for (int r = 0; r < 4; ++r)   // W4: per-token scale, undo x16 (exact)
                                 v[r] = accf[j][i][4 * q + r] * (sav[r] * 0.0625f);
                         }
-                        const int m = mb + q * 8 + out_m;   // rows m .. m+3
                         if (fast) {
 #pragma unroll
-                            for (int h = 0; h < 2; ++h) {    // rows m+2h, m+2h+1
+                            for (int h = 0; h < 2; ++h) {    // rows mb + 8q + out_m + 2h (+1)
                                 const uint32_t w = pair_rows_to_cols(pack_h2(v[2 * h], v[2 * h + 1]),
                                                                      pair_sel);
-                                const int mr = m + 2 * h + (lane & 1);
-                                const int nc = n - (lane & 1);
-                                *reinterpret_cast<uint32_t *>(Y + (int64_t)mr * N + nc) = w;
+                                // wave-uniform row base plus the lane's 32-bit offset
+                                char *row = reinterpret_cast<char *>(
+                                    Y + (int64_t)(mb + q * 8 + 2 * h) * N + nb);
+                                *reinterpret_cast<uint32_t *>(row + lane_off) = w;
                             }
-                        } else if (n < N) {
+                        } else {
+                            const int m = mb + q * 8 + out_m, n = nb + out_n;
+                            if (n < N) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (m + r < M)
-                                    Y[(int64_t)(m + r) * N + n] = f2h(v[r]);
+                                for (int r = 0; r < 4; ++r)
+                                    if (m + r < M)
+                                        Y[(int64_t)(m + r) * N + n] = f2h(v[r]);
+                            }
                         }
                     }
                     // a quarter of the sums at a time: keeps the reads of
@@ -615,7 +636,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         int cm0 = cp.m0, cn0 = cp.n0, ctile = 0;      // the tile being computed
         if constexpr (EW > 0)
             issue_epilogue_scales(cm0, cn0);          // complete before stage 0 does
-        issue_copies(cp, 0, NCW);
+        issue_copies(cp, cp.buf, 0, NCW, KFULL);
         if constexpr (T::int4) {
             w4_load(cp);
             w4_store(0);
@@ -623,9 +644,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         advance(cp);
         if constexpr (T::int4)
             w4_load(cp);
-        issue_copies(cp, 0, NCW);
+        issue_copies(cp, cp.buf, 0, NCW, KFULL);
         advance(cp);
-        issue_copies(cp, 0, CA);
+        issue_copies(cp, cp.buf, 0, CA, KFULL);
         Src c2 = cp;                                  // stage u+2: parts 0-2 in iteration u
         advance(cp);
         Src c3 = cp;                                  // stage u+3: part A in iteration u
@@ -650,16 +671,21 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                     __builtin_amdgcn_sched_barrier(0);
                     if constexpr (T::pergroup) {
                         if constexpr (t % SPG == 0)
-                            mfma_step(cur, std::true_type(), nxt, reads, rbuf, rt, src, c0, n);
+                            mfma_step(cur, std::true_type(), nxt, reads, rbuf, rt, src, src.buf, c0,
+                                      n, KFULL);
                         else
-                            mfma_step(cur, std::false_type(), nxt, reads, rbuf, rt, src, c0, n);
+                            mfma_step(cur, std::false_type(), nxt, reads, rbuf, rt, src, src.buf, c0,
+                                      n, KFULL);
                     } else if constexpr (t == 0) {
                         if (s == 0)                   // a tile's first k-step
-                            mfma_step(cur, std::true_type(), nxt, reads, rbuf, rt, src, c0, n);
+                            mfma_step(cur, std::true_type(), nxt, reads, rbuf, rt, src, src.buf, c0,
+                                      n, KFULL);
                         else
-                            mfma_step(cur, std::false_type(), nxt, reads, rbuf, rt, src, c0, n);
+                            mfma_step(cur, std::false_type(), nxt, reads, rbuf, rt, src, src.buf, c0,
+                                      n, KFULL);
                     } else {
-                        mfma_step(cur, std::false_type(), nxt, reads, rbuf, rt, src, c0, n);
+                        mfma_step(cur, std::false_type(), nxt, reads, rbuf, rt, src, src.buf, c0, n,
+                                  KFULL);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     if constexpr (T::pergroup) {      // close a group if one ends here
@@ -677,7 +703,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                     // (and after the barrier the next stage's fragments) do
                     if constexpr (t == 3)
                         read_frag(nxt, b1, 0);
-                    issue_copies(src, c0, n);
+                    issue_copies(src, src.buf, c0, n, KFULL);
                 }
             };
             step(std::integral_constant<int, 0>(), c2, CA, C0);
