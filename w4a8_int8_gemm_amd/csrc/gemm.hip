@@ -10,12 +10,16 @@
 //
 // Design (CDNA4, wave64, one wave per SIMD for the large tiles):
 //  * One workgroup computes BM x BN tiles of Y (m x n) with WM x WN waves.
-//    Both operands are K-contiguous.  v_mfma_i32_32x32x32_i8 takes the
-//    activation fragment (32 m-rows x 32 k, 16 bytes per lane) as its A
-//    operand and the weight fragment as B, so each lane holds one output
-//    column n and runs of four rows.  This MFMA sustains close to the int8
-//    peak with a single wave per SIMD, which the large per-wave tiles need
-//    (they keep LDS reads per MFMA low).
+//    Both operands are K-contiguous.  v_mfma_i32_32x32x32_i8 multiplies two
+//    32 x 32-k fragments (16 bytes per lane each); a lane of its result holds
+//    one column of the first operand's transpose and runs of four rows.  The
+//    per-channel path puts the weights first, so a lane holds one output row
+//    m and runs of four consecutive columns n, which become 8-byte fp16 runs
+//    (16 bytes after one cross-half lane swap) with no other shuffling; the
+//    per-group and int32 paths put the activations first (one column n, runs
+//    of rows m), which matches their per-column scales and int32 stores.
+//    This MFMA sustains close to the int8 peak with a single wave per SIMD,
+//    which the large per-wave tiles need (they keep LDS reads per MFMA low).
 //  * K advances in stages of 128 bytes through a ring of three LDS buffers.
 //    Stages are copied from global memory straight into LDS (buffer loads
 //    with the lds modifier, 16-byte chunks XOR-swizzled per row); the copies
@@ -81,6 +85,16 @@ __device__ __forceinline__ uint32_t pair_rows_to_cols(uint32_t p, uint32_t sel)
     return __builtin_amdgcn_perm(p, q, sel);
 }
 
+// Swap lanes 32-63 of x with lanes 0-31 of y (v_permlane32_swap): lane l < 32
+// keeps x and receives y of lane l + 32 in y; lane l + 32 receives x of lane l
+// in x and keeps y.
+__device__ __forceinline__ void lane_half_swap(uint32_t &x, uint32_t &y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads stay in
 // flight across it (a full __syncthreads would also wait for them).
 __device__ __forceinline__ void lds_barrier()
@@ -98,6 +112,8 @@ template <GemmMode MODE> struct ModeTraits {
                                       MODE == GemmMode::W4_PARTIALS);
     static constexpr bool fold_sa = (MODE == GemmMode::PG);     // per-group activation scales
     static constexpr bool fold_sw = (MODE == GemmMode::PG || MODE == GemmMode::W4);
+    // weights as the MFMA's first operand: lane = output row, runs along n
+    static constexpr bool nmajor = (MODE == GemmMode::PC);
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -476,8 +492,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 #pragma unroll
         for (int k = 0; k < NM; ++k) {
             const int j = k / FM, i = k % FM;
-            acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.b[i], F.a[j],
-                                                              restart ? v16i{} : acc[j][i], 0, 0, 0);
+            if constexpr (T::nmajor)
+                acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.a[j], F.b[i],
+                                                                  restart ? v16i{} : acc[j][i], 0, 0, 0);
+            else
+                acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.b[i], F.a[j],
+                                                                  restart ? v16i{} : acc[j][i], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (reads) {
 #pragma unroll
@@ -549,6 +569,79 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                 for (int i = 0; i < FM; ++i)
                     store_block_i32(static_cast<int32_t *>(args.out), acc[j][i],
                                     m0 + wm * TM + i * 32, n0 + wn * TN + j * 32, false);
+        } else if constexpr (T::nmajor) {
+            // Lane l holds row m = mw + 32 i + l % 32 of block (i, j); its
+            // accumulator elements 4g..4g+3 are columns nb + 8g + 4 (l / 32) + 0..3.
+            uint16_t *Y = static_cast<uint16_t *>(args.out);
+            const int mw = m0 + wm * TM, nw = n0 + wn * TN;
+            const int lr = lane & 31, lh = lane >> 5;
+            float sam[FM];                       // sa of this lane's rows (clamped at M - 1)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                sam[i] = eps[wm * TM + i * 32 + lr];
+            // whole tile inside the output, rows a multiple of 16 bytes long
+            // and a 16-byte aligned output: every 16-byte store is in bounds
+            // and aligned
+            const bool fast = m0 + BM <= M && n0 + BN <= N && (N & 7) == 0 &&
+                              ((uintptr_t)Y & 15) == 0;
+            if (fast) {
+                // lane's 16-byte piece of a 16-column half row: row lr,
+                // columns 8 lh .. 8 lh + 7 of the half
+                const uint32_t voff = (uint32_t)((lr * N + 8 * lh) * 2);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    v4f swv[4];                  // sw of columns nb + 8g + 4 lh + 0..3
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        swv[g] = *reinterpret_cast<const v4f *>(
+                            &eps[BM + wn * TN + j * 32 + 8 * g + 4 * lh]);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) {
+                        uint32_t d[8];           // fp16 pairs, columns 8g + 4 lh + {0,1}, {2,3}
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            float v[4];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                v[r] = rescale_pc(acc[j][i][4 * g + r], sam[i], swv[g][r]);
+                            d[2 * g] = pack_h2(v[0], v[1]);
+                            d[2 * g + 1] = pack_h2(v[2], v[3]);
+                        }
+                        // trade the upper lanes' group g with the lower lanes'
+                        // group g + 1 (g even): lanes 0-31 then hold columns
+                        // 16 (g/2) + 0..7, lanes 32-63 columns 16 (g/2) + 8..15
+#pragma unroll
+                        for (int g = 0; g < 4; g += 2)
+#pragma unroll
+                            for (int w = 0; w < 2; ++w)
+                                lane_half_swap(d[2 * g + w], d[2 * g + 2 + w]);
+                        // wave-uniform block base plus the lane's 32-bit offset
+                        char *blk = reinterpret_cast<char *>(
+                            Y + (int64_t)(mw + i * 32) * N + nw + j * 32) + voff;
+                        *reinterpret_cast<v4u *>(blk) = v4u{d[0], d[1], d[2], d[3]};
+                        *reinterpret_cast<v4u *>(blk + 32) = v4u{d[4], d[5], d[6], d[7]};
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) {
+                        const int m = mw + i * 32 + lr;
+                        if (m < M) {
+#pragma unroll
+                            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const int nl = wn * TN + j * 32 + 8 * g + 4 * lh + r;
+                                    if (n0 + nl < N)
+                                        Y[(int64_t)m * N + n0 + nl] =
+                                            f2h(rescale_pc(acc[j][i][4 * g + r], sam[i], eps[BM + nl]));
+                                }
+                        }
+                    }
+            }
         } else if constexpr (!T::partials) {
             uint16_t *Y = static_cast<uint16_t *>(args.out);
             // whole tile inside the output and rows of an even length: every
@@ -558,12 +651,6 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
             // lanes write row m at columns n, n+1; odd lanes row m+1 at n-1, n
             const uint32_t lane_off =
                 (uint32_t)(((out_m + (lane & 1)) * N + out_n - (lane & 1)) * 2);
-            float swn[FN];
-            if constexpr (MODE == GemmMode::PC) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j)   // sw[n] (clamped at N - 1 by the scale copies)
-                    swn[j] = eps[BM + wn * TN + j * 32 + out_n];
-            }
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int mb = m0 + wm * TM + i * 32;
@@ -577,11 +664,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                     for (int j = 0; j < FN; ++j) {
                         const int nb = n0 + wn * TN + j * 32;
                         float v[4];
-                        if constexpr (MODE == GemmMode::PC) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                v[r] = rescale_pc(acc[j][i][4 * q + r], sav[r], swn[j]);
-                        } else if constexpr (MODE == GemmMode::PG) {
+                        if constexpr (MODE == GemmMode::PG) {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
                                 v[r] = accf[j][i][4 * q + r];
