@@ -24,6 +24,10 @@ PC_SHAPES = [
     (16, 512, 256), (1, 96, 64), (3, 100, 192), (64, 64, 64),
     (65, 130, 320), (200, 300, 192), (257, 321, 256),
     (1024, 4096, 128), (2048, 8192, 128), (2048, 10240, 128), (1500, 10240, 192),
+    # 256x128 tiles (N not a multiple of 160) with ragged M and N: whole
+    # stages only, rows not a multiple of 16 bytes (scalar stores), few
+    # stages per tile, a K tail
+    (2000, 8200, 1024), (1800, 8196, 1280), (2048, 8192, 512), (2000, 8200, 320),
 ]
 
 

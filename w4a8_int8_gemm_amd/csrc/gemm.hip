@@ -159,16 +159,23 @@ __device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes)
     return r;
 }
 
-// 16 bytes per lane from a buffer resource into LDS at M0 + 16 * lane, from
-// byte offset voff + soff of the resource.  Lanes whose voff lies past the
-// resource's size read zeros.
-__device__ __forceinline__ void copy16_buf_to_lds(v4i rsrc, uint32_t voff, uint32_t soff,
-                                                  uint32_t lds)
+// M0 = the LDS address the next direct-to-LDS buffer loads write at.
+__device__ __forceinline__ void set_m0(uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
-                 "buffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" : : "s"(lds) : "memory");
+}
+
+// 16 bytes per lane from a buffer resource into LDS at M0 + OFF + 16 * lane,
+// from byte offset voff + OFF (+ soff) of the resource.  The immediate OFF
+// adds to both addresses and takes part in the range check: lanes whose
+// voff + OFF lies past the resource's size read zeros.  M0 must hold the
+// LDS base (set_m0); nothing else in these kernels touches M0.
+template <int OFF>
+__device__ __forceinline__ void copy16_buf_to_lds(v4i rsrc, uint32_t voff, uint32_t soff)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
                  :
-                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF)
                  : "memory");
 }
 
@@ -178,6 +185,15 @@ __device__ __forceinline__ void copy16_buf_to_lds(v4i rsrc, uint32_t voff, uint3
 // b).  Its K-stages form one stream across its tiles, so the copies of the
 // next tile's first stages are in flight while the current tile finishes and
 // writes its outputs.
+// Size of the p-th non-empty window of w[0..3] (0 past the last one).
+constexpr int part_of_windows(const int (&w)[4], int p)
+{
+    for (int i = 0; i < 4; ++i)
+        if (w[i] != 0 && p-- == 0)
+            return w[i];
+    return 0;
+}
+
 template <int BM, int BN, int WM, int WN, GemmMode MODE, int GS>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int tiles_m,
                                                            int tiles_n, int group_m)
@@ -194,7 +210,6 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     constexpr bool kDmaW = !T::int4;                  // int8 weights go straight to LDS
     constexpr int WB = kDmaW ? WBUF / 1024 / NW : 0;
     static_assert(!kDmaW || WBUF % (1024 * NW) == 0, "W stage must split evenly over the waves");
-    constexpr int RB = XB > WB ? XB : WB;             // distinct row offsets per lane
     // packed int4 weights are staged through registers and unpacked
     constexpr int WCH4 = BN * 4;                      // 16-byte packed chunks per stage
     constexpr int WIT4 = T::int4 ? (WCH4 + NW * 64 - 1) / (NW * 64) : 0;
@@ -217,11 +232,16 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     // in that buffer).  int4 weights are register-staged; their compiler
     // tracked loads make it wait for every earlier copy before the unpack, so
     // there the tile copies all go in part A and the scale copies in part 0.
+    // Tile copies go in windows of up to four consecutive 1 KiB blocks that
+    // share one M0 value (see issue_copy); without scale copies each part is
+    // one window: X blocks 0-3, X 4-7, W 0-3, W 4-7 (empty windows dropped).
     constexpr int NCP = NCW / 4, NCR = NCW % 4;
-    constexpr int CA = T::int4 ? XB + WB : NCP + (NCR > 0);
-    constexpr int C0 = T::int4 ? NCW - CA : NCP + (NCR > 1);
-    constexpr int C1 = T::int4 ? 0 : NCP + (NCR > 2);
-    constexpr int C2 = T::int4 ? 0 : NCP;
+    constexpr bool WSPLIT = !T::pergroup && !T::int4 && XB <= 8 && WB <= 8;
+    constexpr int WIN[4] = {XB < 4 ? XB : 4, XB < 4 ? 0 : XB - 4, WB < 4 ? WB : 4, WB < 4 ? 0 : WB - 4};
+    constexpr int CA = WSPLIT ? part_of_windows(WIN, 0) : T::int4 ? XB + WB : NCP + (NCR > 0);
+    constexpr int C0 = WSPLIT ? part_of_windows(WIN, 1) : T::int4 ? NCW - CA : NCP + (NCR > 1);
+    constexpr int C1 = WSPLIT ? part_of_windows(WIN, 2) : T::int4 ? 0 : NCP + (NCR > 2);
+    constexpr int C2 = WSPLIT ? part_of_windows(WIN, 3) : T::int4 ? 0 : NCP;
     static_assert(CA + C0 + C1 + C2 == NCW, "copy split");
     static_assert(!T::pergroup || CA <= XB + WB, "scale copies must not go in part A");
     // epilogue scales staged in LDS: per-token sa (PC, W4) followed by
@@ -276,17 +296,31 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 
     // Direct-to-LDS copies.  A wave instruction writes lane l's 16 bytes at
     // LDS block + 16*l, i.e. row 8*blk + l/8, physical chunk l%8; the lane
-    // therefore fetches the logical chunk that the swizzle puts there.  Byte
-    // offsets within a tile (X and int8 W rows are both K bytes long); rows
-    // past the end of the matrix fall outside the tile's buffer resource and
-    // read as zeros.
+    // therefore fetches the logical chunk that the swizzle puts there.  Wave w
+    // copies the X blocks w*XB .. w*XB + XB - 1 of a stage and the W blocks
+    // w*WB .., in windows of four blocks (32 rows) whose copies share one M0
+    // value: copy q of a window reaches its block through the instruction
+    // offset 1024 q, which moves the global address by the same amount, so
+    // the lane offset carries -1024 q (whole stages; with a K tail the
+    // offset is 0 and M0 moves per copy).  Window h adds 32 h rows to the
+    // lane offset.  Byte offsets within a tile; rows past the end of the
+    // matrix fall outside the tile's buffer resource (the instruction offset
+    // takes part in the range check) and read as zeros.
     const int dma_row = lane >> 3;
-    uint32_t vrow[RB];
+    auto lane_off = [&](int nb, int q, bool shifted) __attribute__((always_inline)) {
+        // row 8 (w*nb + q) + l/8 of the tile, the swizzle parity of block w*nb + q
+        const int row = (wave * nb + q) * 8 + dma_row;
+        const int c = (lane & 7) ^ dma_row ^ ((wave * nb + q) & 1);
+        return (uint32_t)(row * K + c * 16 - (shifted ? 1024 * q : 0));
+    };
+    uint32_t vqx[XB < 4 ? XB : 4], vqw[WB == 0 ? 1 : (WB < 4 ? WB : 4)];
+    const bool kwhole = K % BK == 0;
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-        const int row = (wave + NW * i) * 8 + dma_row;
-        vrow[i] = (uint32_t)(row * K + swz(row, lane & 7) * 16);
-    }
+    for (int q = 0; q < (XB < 4 ? XB : 4); ++q)
+        vqx[q] = lane_off(XB, q, kwhole);
+#pragma unroll
+    for (int q = 0; q < (WB < 4 ? WB : 4); ++q)
+        vqw[q] = lane_off(WB, q, kwhole);
 
     // Where the copies of one stage come from: the stage's tile, its index
     // within the tile and the LDS buffer it goes to.  Wave-uniform.
@@ -321,18 +355,35 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     // The stage's K offset goes in the scalar offset when K % 128 == 0 (every
     // stage is whole, so a row's bytes never run past its end); for a K tail
     // it is added to the per-lane offset, which the resource's range check
-    // covers.
-    auto issue_copy = [&](const Src &src, int buf, int c, auto KFULL) __attribute__((always_inline)) {
+    // covers.  `first`: the first copy of a run (M0 is set again).
+    auto issue_copy = [&](const Src &src, int buf, int c, bool first, auto KFULL)
+                          __attribute__((always_inline)) {
         constexpr bool kfull = decltype(KFULL)::value;
         const uint32_t k0 = (uint32_t)(src.s * BK);
-        const uint32_t vk = kfull ? 0u : k0, sk = kfull ? k0 : 0u;
-        if (c < XB) {
-            copy16_buf_to_lds(src.rx, vrow[c] + vk, sk,
-                              lds_addr(xs + buf * XBUF + (wave + NW * c) * 1024));
-        } else if (c < XB + WB) {
-            const int i = c - XB;
-            copy16_buf_to_lds(src.rw, vrow[i] + vk, sk,
-                              lds_addr(ws + buf * WBUF + (wave + NW * i) * 1024));
+        if (c < XB + WB) {
+            const bool isx = c < XB;
+            const int nb = isx ? XB : WB;
+            const int i = isx ? c : c - XB;
+            const int q = i % 4, h = i / 4;
+            const int blk0 = wave * nb + 4 * h;       // the window's first block
+            const v4i r = isx ? src.rx : src.rw;
+            const uint32_t lds = lds_addr((isx ? xs + buf * XBUF : ws + buf * WBUF) + blk0 * 1024);
+            const uint32_t voff = (isx ? vqx[q] : vqw[q]) + (uint32_t)(h * 32 * K);
+            if constexpr (kfull) {
+                if (first || q == 0)
+                    set_m0(lds);
+                if (q == 0)
+                    copy16_buf_to_lds<0>(r, voff, k0);
+                else if (q == 1)
+                    copy16_buf_to_lds<1024>(r, voff, k0);
+                else if (q == 2)
+                    copy16_buf_to_lds<2048>(r, voff, k0);
+                else
+                    copy16_buf_to_lds<3072>(r, voff, k0);
+            } else {
+                set_m0(lds + 1024 * q);
+                copy16_buf_to_lds<0>(r, voff + k0, 0u);
+            }
         } else if (c < XB + WB + SAW) {
             if constexpr (T::fold_sa) {
                 const int ins = wave + NW * (c - XB - WB);
@@ -365,7 +416,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 #pragma unroll
         for (int c = 0; c < NCW; ++c)
             if (c >= c0 && c < c0 + n)
-                issue_copy(src, buf, c, KFULL);
+                issue_copy(src, buf, c, c == c0, KFULL);
     };
     // The epilogue scales of the tile at (m0, n0); rows and columns past the
     // end repeat the last one.
@@ -508,7 +559,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 #pragma unroll
             for (int p = 0; p < NCW; ++p)
                 if (p < n && k == ((2 * p + 1) * NM) / (2 * n))
-                    issue_copy(src, sbuf, c0 + p, KFULL);
+                    issue_copy(src, sbuf, c0 + p, p == 0, KFULL);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
