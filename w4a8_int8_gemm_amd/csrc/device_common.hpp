@@ -108,33 +108,61 @@ __device__ __forceinline__ uint32_t absmax_bits8(uint4 v)
     return max(max(m0, m1), max(m2, m3));
 }
 
+// fl32(x r) for the fp16 x in the low (HI false) or high half of w, in one
+// v_fma_mix_f32: the fp16 converts exactly and the addend is +0, so the
+// result is the rounded product (a zero product comes out as +0).
+template <bool HI>
+__device__ __forceinline__ float h2f_times(uint32_t w, float r)
+{
+    float t;
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(t) : "v"(w), "v"(r));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(t) : "v"(w), "v"(r));
+    return t;
+}
+
+// Bytes 0 of the bit patterns of a, b, c, d as one dword (a lowest).
+__device__ __forceinline__ uint32_t low_bytes4(float a, float b, float c, float d)
+{
+    const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x04000c0cu);
+    return ab | cd;
+}
+
 // Quantize the eight fp16 values of a chunk with scale s (r = fl32(1/s)).
-// Fast path for all eight; if any of them is guarded, the whole chunk goes
-// through the division rule.  Returns the eight codes as two dwords.
+// Fast path for all eight: t = fl32(x r); m = t + 1.5 * 2^23 rounds t to the
+// nearest integer (ties to even, |t| < 2^22) and holds it, two's complement,
+// in its low mantissa bits, so byte 0 of m is the code and m - 1.5 * 2^23
+// (exact) is rint(t) for the guard.  If any of the eight is guarded, the
+// whole chunk goes through the division rule.  Returns the codes as two
+// dwords.
 __device__ __forceinline__ uint2 quant_chunk8(uint4 v, float s, float r, float qmax)
 {
     if (s == 0.0f)
         return make_uint2(0u, 0u);
-    float x[8] = {lo_h2f(v.x), hi_h2f(v.x), lo_h2f(v.y), hi_h2f(v.y),
-                  lo_h2f(v.z), hi_h2f(v.z), lo_h2f(v.w), hi_h2f(v.w)};
-    float t[8];
+    constexpr float kRound = 0x1.8p23f;
+    const float t[8] = {h2f_times<false>(v.x, r), h2f_times<true>(v.x, r),
+                        h2f_times<false>(v.y, r), h2f_times<true>(v.y, r),
+                        h2f_times<false>(v.z, r), h2f_times<true>(v.z, r),
+                        h2f_times<false>(v.w, r), h2f_times<true>(v.w, r)};
+    float m[8];
     float far = 0.0f;                 // largest distance to an integer
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        t[i] = quant_fast_t(x[i], r);
-        far = fmaxf(far, quant_fast_resid(t[i]));
+        m[i] = t[i] + kRound;
+        far = fmaxf(far, fabsf(t[i] - (m[i] - kRound)));
     }
-    int q[8];
     if (__builtin_expect(quant_fast_slow(far), 0)) {
+        const float x[8] = {lo_h2f(v.x), hi_h2f(v.x), lo_h2f(v.y), hi_h2f(v.y),
+                            lo_h2f(v.z), hi_h2f(v.z), lo_h2f(v.w), hi_h2f(v.w)};
+        int q[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             q[i] = quant_code_div(x[i], s, qmax);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            q[i] = quant_fast_code(t[i]);
+        return make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]));
     }
-    return make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]));
+    return make_uint2(low_bytes4(m[0], m[1], m[2], m[3]), low_bytes4(m[4], m[5], m[6], m[7]));
 }
 
 // Per-channel rescale of one int32 sum; the same operation order everywhere
