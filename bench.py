@@ -174,6 +174,48 @@ def suite(reps):
             print(rows[-1], flush=True)
             del x, y, wq, sw, xq, xs
             torch.cuda.empty_cache()
+    # decode (M = 1) with per-group weight scales: the matrix-vector kernels,
+    # warm and (for the kernel trace) cold, against quantize_act + the mode's
+    # GEMM at M = 1
+    for mode, gs, N, K in [("pg", 128, 14336, 4096), ("pg", 64, 14336, 4096),
+                           ("pg", 128, 4096, 14336), ("w4a8", 128, 6144, 4096),
+                           ("w4a8", 128, 24576, 4096), ("w4a8", 128, 4096, 12288)]:
+        x = torch.from_numpy(synth.activations(1, K, seed=1)).cuda()
+        wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
+        if mode == "w4a8":
+            wq, sw = w.pack_weight_int4(wt, gs)
+            mv = lambda: w.check(L.w4a8_mv(ptr(x), ptr(wq), ptr(sw), gs, ptr(y), N, K, sp))
+        else:
+            wq, sw = w.quantize_weight_int8(wt, gs)
+            mv = lambda: w.check(L.w8a8_mv_pg(ptr(x), ptr(wq), ptr(sw), gs, ptr(y), N, K, sp))
+        del wt
+        y = torch.empty((N,), dtype=torch.float16, device="cuda")
+        act_gs = gs if mode == "pg" else 0
+        xq = torch.empty((1, K), dtype=torch.int8, device="cuda")
+        xs = torch.empty((1, K // act_gs if act_gs else 1), dtype=torch.float32, device="cuda")
+        q = lambda: w.check(L.quantize_act(ptr(x), 1, K, act_gs, ptr(xq), ptr(xs), sp))
+        if mode == "w4a8":
+            g = lambda: w.check(L.w4a8_gemm(ptr(xq), ptr(xs), ptr(wq), ptr(sw), gs, ptr(y), 1, N,
+                                            K, sp))
+        else:
+            g = lambda: w.check(L.w8a8_gemm_pg(ptr(xq), ptr(xs), ptr(wq), ptr(sw), gs, ptr(y), 1,
+                                               N, K, sp))
+        us = b2b(mv)
+        path_us = b2b(q) + b2b(g)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for _ in range(reps):
+            flush.fill_(1)
+            mv()
+        torch.cuda.synchronize()
+        del flush
+        wbytes = wq.numel() + sw.numel() * 4 + 2 * K + 2 * N
+        kern = "w4a8_mv" if mode == "w4a8" else "w8a8_mv_pg"
+        rows.append(f"{mode + '_mv':10s} M=    1 N={N:5d} K={K:5d}  {kern} gs={gs} {us:8.2f} us warm  "
+                    f"{wbytes / us / 1e3:7.0f} GB/s ({100 * wbytes / us / 1e3 / PEAK_HBM_GBS:.0f}% "
+                    f"of HBM peak) | quantize + GEMM at M=1 {path_us:8.2f} us")
+        print(rows[-1], flush=True)
+        del x, y, wq, sw, xq, xs
+        torch.cuda.empty_cache()
     print("\n".join(rows), flush=True)
 
 

@@ -148,15 +148,35 @@ w4a8_status_t int8_mv(const w4a8_f16 *x, const int8_t *wq, const float *w_scale,
                       int64_t N, int64_t K, int8_t *xq_out, float *x_scale_out,
                       w4a8_stream_t stream);
 
+/* Decode matrix-vector products with per-group weight scales (the decode
+ * side of the per-group and W4A8 modes; [P2] file list: a per-group W8A8 MV
+ * next to the per-channel one).  Same results as quantize_act + the mode's
+ * GEMM at M = 1, up to the fp32 summation order (within the per-group
+ * tolerance of the GEMMs):
+ *   w8a8_mv_pg: the token is quantized per group of group_size (x_scale[g]);
+ *       y[n] = fp16( sum_g P_g[n] * x_scale[g] * w_scale[n,g] ),
+ *       wq int8 [N, K], w_scale fp32 [N, K/gs].
+ *   w4a8_mv: the token is quantized per token (scale s);
+ *       y[n] = fp16( s * sum_g P_g[n] * w_scale[n,g] ),
+ *       w4 uint8 [N, K/2] (layout above), w_scale fp32 [N, K/gs].
+ * P_g[n] = sum over k in group g of q[k] * w[n,k] (exact int32).  x fp16
+ * [K], y fp16 [N].  group_size 64 or 128; K a multiple of 64 and of
+ * group_size, 0 < K <= 32768.  N == 0 returns W4A8_OK with no launch. */
+w4a8_status_t w8a8_mv_pg(const w4a8_f16 *x, const int8_t *wq, const float *w_scale,
+                         int32_t group_size, w4a8_f16 *y, int64_t N, int64_t K,
+                         w4a8_stream_t stream);
+w4a8_status_t w4a8_mv(const w4a8_f16 *x, const uint8_t *w4, const float *w_scale,
+                      int32_t group_size, w4a8_f16 *y, int64_t N, int64_t K,
+                      w4a8_stream_t stream);
+
 /* Bytes of device workspace linear() needs for these sizes (int8 codes and
  * fp32 scales of the activations, each 256-byte aligned).  0 when M == 0, and
- * for M == 1 in per-channel mode with K <= 32768 (the matrix-vector path
- * needs none). */
+ * for M == 1 with K <= 32768 (the matrix-vector paths need none). */
 size_t linear_workspace_size(w4a8_mode_t mode, int64_t M, int64_t K, int32_t group_size);
 
-/* The whole layer with path selection ([P2] path selection): M == 1 in
- * per-channel mode runs int8_mv (K <= 32768); otherwise quantize_act then the
- * mode's GEMM.  What linear accepts does not depend on M: the GEMM's rules.
+/* The whole layer with path selection ([P2] path selection): M == 1 runs the
+ * mode's matrix-vector kernel (int8_mv, w8a8_mv_pg or w4a8_mv; K <= 32768);
+ * otherwise quantize_act then the mode's GEMM.  What linear accepts does not depend on M: the GEMM's rules.
  * x fp16 [M, K]; w is int8 [N, K] (PC, PG) or packed uint8 [N, K/2] (W4A8);
  * w_scale as the mode's GEMM takes it; group_size is ignored in PC mode.
  * workspace: device buffer of at least linear_workspace_size() bytes, 256-byte

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for fn in ["quantize_act", "w8a8_gemm_pc", "w8a8_gemm_pg", "w4a8_gemm", "int8_mv", "linear",
                "quantize_weight_int8", "pack_weight_int4", "w4a8_is_available",
                "w4a8_status_string", "w4a8_last_error", "linear_workspace_size",
-               "w8a8_gemm_i32", "w8a8_gemm_pg_partials", "w4a8_gemm_partials"]:
+               "w8a8_gemm_i32", "w8a8_gemm_pg_partials", "w4a8_gemm_partials",
+               "w8a8_mv_pg", "w4a8_mv"]:
         assert fn in names, fn
 
 
@@ -92,6 +93,19 @@ def _last():
     (lambda L: L.int8_mv(A, A2, A3, A4, 8, 32784, None, None, None), w.Status.ERR_SHAPE),
     (lambda L: L.int8_mv(None, A2, A3, A4, 8, 64, None, None, None), w.Status.ERR_INVALID_ARG),
     (lambda L: L.int8_mv(A, A2, A3, A4, 0, 64, None, None, None), w.Status.OK),
+    # w8a8_mv_pg / w4a8_mv(x, w, sw, gs, y, N, K, stream)
+    (lambda L: L.w8a8_mv_pg(A, A2, A3, 32, A4, 8, 256, None), w.Status.ERR_SHAPE),
+    (lambda L: L.w8a8_mv_pg(A, A2, A3, 128, A4, 8, 320, None), w.Status.ERR_SHAPE),
+    (lambda L: L.w8a8_mv_pg(A, A2, A3, 64, A4, 8, 32832, None), w.Status.ERR_SHAPE),
+    (lambda L: L.w8a8_mv_pg(None, A2, A3, 64, A4, 8, 256, None), w.Status.ERR_INVALID_ARG),
+    (lambda L: L.w8a8_mv_pg(A, None, A3, 64, A4, 8, 256, None), w.Status.ERR_INVALID_ARG),
+    (lambda L: L.w8a8_mv_pg(A, MIS, A3, 64, A4, 8, 256, None), w.Status.ERR_ALIGNMENT),
+    (lambda L: L.w8a8_mv_pg(A, A2, A3, 64, A4, 0, 256, None), w.Status.OK),
+    (lambda L: L.w4a8_mv(A, A2, A3, 0, A4, 8, 256, None), w.Status.ERR_SHAPE),
+    (lambda L: L.w4a8_mv(A, A2, A3, 128, A4, 8, 192, None), w.Status.ERR_SHAPE),
+    (lambda L: L.w4a8_mv(MIS, A2, A3, 128, A4, 8, 256, None), w.Status.ERR_ALIGNMENT),
+    (lambda L: L.w4a8_mv(A, A2, A3, 128, A4, -1, 256, None), w.Status.ERR_INVALID_ARG),
+    (lambda L: L.w4a8_mv(A, A2, A3, 128, A4, 0, 256, None), w.Status.OK),
     # linear(mode, x, M, K, w, sw, gs, N, y, ws, ws_bytes, stream)
     (lambda L: L.linear(7, A, 4, 256, A2, A3, 0, 8, A4, A5, 1 << 20, None), w.Status.ERR_INVALID_ARG),
     (lambda L: L.linear(0, A, 4, 256, A2, A3, 0, 8, A4, None, 0, None), w.Status.ERR_WORKSPACE),
@@ -115,6 +129,9 @@ def test_workspace_size():
     assert L.linear_workspace_size(1, 4096, 4096, 64) == a256(4096 * 4096) + a256(4096 * 64 * 4)
     assert L.linear_workspace_size(2, 4516, 4096, 128) == a256(4516 * 4096) + a256(4516 * 4)
     assert L.linear_workspace_size(0, 1, 2560, 0) == 0
+    assert L.linear_workspace_size(1, 1, 4096, 128) == 0      # decode: matrix-vector kernels
+    assert L.linear_workspace_size(2, 1, 4096, 64) == 0
+    assert L.linear_workspace_size(1, 1, 65536, 128) == a256(65536) + a256(512 * 4)
     assert L.linear_workspace_size(0, 0, 2560, 0) == 0
 
 

@@ -9,17 +9,19 @@ library's HIP kernels; nothing here computes.
     wq, sw = quantize_weight_int8(w)               # offline, per output channel
     y = w8a8_gemm_pc(xq, xs, wq, sw)               # fp16 [M, N]
     y = linear(Mode.W8A8_PC, x, wq, sw)            # the whole layer, MV when M == 1
+    y = w8a8_mv_pg(x1, wq, sw, 128)                # decode with per-group scales
 """
 from __future__ import annotations
 
 from ._lib import LIB_PATH, Mode, Status, W4A8Error, check, lib
 from .ops import (int8_mv, is_available, linear, linear_workspace_size, pack_weight_int4,
                   quantize_act, quantize_weight_int8, w4a8_gemm, w4a8_gemm_partials,
-                  w8a8_gemm_i32, w8a8_gemm_pc, w8a8_gemm_pg, w8a8_gemm_pg_partials)
+                  w4a8_mv, w8a8_gemm_i32, w8a8_gemm_pc, w8a8_gemm_pg, w8a8_gemm_pg_partials,
+                  w8a8_mv_pg)
 
 __all__ = [
     "LIB_PATH", "Mode", "Status", "W4A8Error", "check", "lib", "int8_mv", "is_available",
     "linear", "linear_workspace_size", "pack_weight_int4", "quantize_act",
     "quantize_weight_int8", "w4a8_gemm", "w4a8_gemm_partials", "w8a8_gemm_i32",
-    "w8a8_gemm_pc", "w8a8_gemm_pg", "w8a8_gemm_pg_partials",
+    "w8a8_gemm_pc", "w8a8_gemm_pg", "w8a8_gemm_pg_partials", "w4a8_mv", "w8a8_mv_pg",
 ]

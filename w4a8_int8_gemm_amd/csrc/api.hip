@@ -164,6 +164,23 @@ w4a8_status_t check_mv(const void *x, const void *w, const float *sw, const void
     return W4A8_OK;
 }
 
+w4a8_status_t check_mv_group(const char *fn, const void *x, const void *w, const float *sw,
+                             const void *y, int64_t N, int64_t K, int32_t gs)
+{
+    if (N < 0 || K < 0 || N > kMaxDim)
+        return fail(W4A8_ERR_INVALID_ARG, "%s: sizes out of range", fn);
+    if (gs != 64 && gs != 128)
+        return fail(W4A8_ERR_SHAPE, "%s: group_size %d must be 64 or 128", fn, (int)gs);
+    if (K == 0 || K % 64 != 0 || K % gs != 0 || K > kMaxKMv)
+        return fail(W4A8_ERR_SHAPE, "%s: K=%lld must be a multiple of 64 and of group_size in "
+                    "(0, %lld]", fn, (long long)K, (long long)kMaxKMv);
+    if (!x || (N > 0 && (!w || !sw || !y)))
+        return fail(W4A8_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned16(x) || (N > 0 && (!aligned16(w) || !aligned4(sw) || !aligned4(y))))
+        return fail(W4A8_ERR_ALIGNMENT, "%s: misaligned tensor", fn);
+    return W4A8_OK;
+}
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 GemmArgs make_args(const int8_t *xq, const float *sa, const void *w, const float *sw, void *out,
@@ -311,11 +328,44 @@ w4a8_status_t int8_mv(const w4a8_f16 *x, const int8_t *wq, const float *w_scale,
     return check_launch("int8_mv");
 }
 
+w4a8_status_t w8a8_mv_pg(const w4a8_f16 *x, const int8_t *wq, const float *w_scale,
+                         int32_t group_size, w4a8_f16 *y, int64_t N, int64_t K,
+                         w4a8_stream_t stream)
+{
+    w4a8_status_t st = check_mv_group("w8a8_mv_pg", x, wq, w_scale, y, N, K, group_size);
+    if (st != W4A8_OK)
+        return st;
+    if (N == 0)
+        return ok();
+    st = check_device();
+    if (st != W4A8_OK)
+        return st;
+    launch_mv_group(false, group_size, x, reinterpret_cast<const uint8_t *>(wq), w_scale, y,
+                    (int)N, (int)K, (hipStream_t)stream);
+    return check_launch("w8a8_mv_pg");
+}
+
+w4a8_status_t w4a8_mv(const w4a8_f16 *x, const uint8_t *w4, const float *w_scale,
+                      int32_t group_size, w4a8_f16 *y, int64_t N, int64_t K,
+                      w4a8_stream_t stream)
+{
+    w4a8_status_t st = check_mv_group("w4a8_mv", x, w4, w_scale, y, N, K, group_size);
+    if (st != W4A8_OK)
+        return st;
+    if (N == 0)
+        return ok();
+    st = check_device();
+    if (st != W4A8_OK)
+        return st;
+    launch_mv_group(true, group_size, x, w4, w_scale, y, (int)N, (int)K, (hipStream_t)stream);
+    return check_launch("w4a8_mv");
+}
+
 size_t linear_workspace_size(w4a8_mode_t mode, int64_t M, int64_t K, int32_t group_size)
 {
     if (M <= 0 || K <= 0)
         return 0;
-    if (mode == W4A8_MODE_W8A8_PC && M == 1 && K <= kMaxKMv)
+    if (M == 1 && K <= kMaxKMv)                   // the matrix-vector kernels need none
         return 0;
     int64_t groups = 1;
     if (mode == W4A8_MODE_W8A8_PG && group_size > 0)
@@ -340,9 +390,19 @@ w4a8_status_t linear(w4a8_mode_t mode, const w4a8_f16 *x, int64_t M, int64_t K, 
         return ok();
     if (!x || !aligned16(x))
         return fail(x ? W4A8_ERR_ALIGNMENT : W4A8_ERR_INVALID_ARG, "linear: bad x");
-    if (mode == W4A8_MODE_W8A8_PC && M == 1 && K <= kMaxKMv)
-        return int8_mv(x, static_cast<const int8_t *>(w), w_scale, y, N, K, nullptr, nullptr,
-                       stream);
+    if (M == 1 && K <= kMaxKMv) {                 // decode: the matrix-vector kernels
+        switch (mode) {
+        case W4A8_MODE_W8A8_PC:
+            return int8_mv(x, static_cast<const int8_t *>(w), w_scale, y, N, K, nullptr, nullptr,
+                           stream);
+        case W4A8_MODE_W8A8_PG:
+            return w8a8_mv_pg(x, static_cast<const int8_t *>(w), w_scale, group_size, y, N, K,
+                              stream);
+        default:
+            return w4a8_mv(x, static_cast<const uint8_t *>(w), w_scale, group_size, y, N, K,
+                           stream);
+        }
+    }
     const size_t need = linear_workspace_size(mode, M, K, group_size);
     if (!workspace || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)

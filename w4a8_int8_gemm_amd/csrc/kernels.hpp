@@ -41,4 +41,9 @@ void launch_gemm(GemmMode mode, const GemmArgs &a, hipStream_t st);
 void launch_int8_mv(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, int N,
                     int K, int8_t *xq_out, float *xs_out, hipStream_t st);
 
+// Decode matrix-vector with per-group weight scales: per-group W8A8 (token
+// quantized per group of gs) or W4A8 (packed int4 weights, per-token scale).
+void launch_mv_group(bool int4, int gs, const uint16_t *x, const uint8_t *w, const float *sw,
+                     uint16_t *y, int N, int K, hipStream_t st);
+
 }  // namespace w4a8

@@ -144,6 +144,224 @@ void launch_x(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, 
     }
 }
 
+
+// fp32 sum over groups of `width` consecutive lanes (16 or 64), with the
+// DPP moves of lane_reduce on the bit patterns (a lane a move does not reach
+// takes +0).
+template <int width>
+__device__ __forceinline__ float group_sum_f32(float v)
+{
+#define W4A8_DPPF(x, ctrl, rows) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctrl), (rows), 0xf, false))
+    static_assert(width == 16 || width == 64, "reduction width");
+    v += W4A8_DPPF(v, 0xb1, 0xf);
+    v += W4A8_DPPF(v, 0x4e, 0xf);
+    v += W4A8_DPPF(v, 0x141, 0xf);
+    v += W4A8_DPPF(v, 0x140, 0xf);
+    if constexpr (width == 64) {
+        v += W4A8_DPPF(v, 0x142, 0xa);
+        v += W4A8_DPPF(v, 0x143, 0xc);
+        v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    }
+#undef W4A8_DPPF
+    return v;
+}
+
+// Decode with per-group weight scales: the per-group W8A8 mode (the token is
+// quantized per group of GS as well) and W4A8 (packed int4 weights, one
+// scale for the token).  A 16-byte weight chunk (16 int8 or 32 int4 codes)
+// lies inside one group; the CPG lanes holding the chunks of a group add
+// their int32 dot products (exact), and the group's first lane folds the
+// sum into its fp32 accumulator with the group's scales in the GEMM's
+// operation order (fma of the sum with sa*sw, or with sw for int4); the
+// row's lanes then add their accumulators.  int4 codes are used as
+// 16 * code (the nibble moved into the high half of a byte), so the token's
+// codes are staged split into even and odd k to meet the low and high
+// nibbles of each weight byte; the factor 16 is undone at the end (exact).
+template <bool INT4, int GS, int LPR, int CPL, int XCH>
+__global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restrict__ x,
+                                                       const uint8_t *__restrict__ w,
+                                                       const float *__restrict__ sw,
+                                                       uint16_t *__restrict__ y, int N, int K)
+{
+    // LDS: the token's codes (K bytes), then its per-group scales (per-group
+    // mode, K/GS floats)
+    extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+    __shared__ uint32_t red[4];
+    constexpr int RPB = 256 / LPR;                  // rows per workgroup
+    constexpr int KPC = INT4 ? 32 : 16;             // k per 16-byte weight chunk
+    constexpr int CPG = GS / KPC;                   // chunks per group
+    static_assert(CPG == 2 || CPG == 4 || CPG == 8, "chunks per group");
+    const int G = K / GS;
+    int8_t *xq_s = smem;
+    float *sa_s = reinterpret_cast<float *>(smem + K);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * RPB;
+    const int rl = tid / LPR, lr = tid % LPR;
+    const int n = n0 + rl;
+    const int rowb = INT4 ? K / 2 : K;              // bytes per weight row
+    const int nch = rowb >> 4;
+    const uint4 *wr = reinterpret_cast<const uint4 *>(w + (int64_t)min(n, N - 1) * rowb);
+    const float *swr = sw + (int64_t)min(n, N - 1) * G;    // the row's group scales
+    const bool leader = lr % CPG == 0;              // first lane of its group's lanes
+
+    // 1. this thread's chunks of the token (8 fp16 each): c = tid + 256 j
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x);
+    const int nx = K >> 3;
+    uint4 xv[XCH];
+#pragma unroll
+    for (int j = 0; j < XCH; ++j) {
+        const int c = tid + 256 * j;
+        xv[j] = c < nx ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // 2. first batch of weight loads in flight, with the group scales the
+    // leading lanes fold them with
+    uint4 wv[CPL];
+    float swv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lr + LPR * j;
+        wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lr + LPR * j;
+        swv[j] = (leader && c < nch) ? swr[c / CPG] : 0.0f;
+    }
+
+    // 3. the token's scale(s) and codes
+    float s = 0.0f;                                 // the token's scale (int4)
+    if constexpr (INT4) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < XCH; ++j)
+            m = max(m, absmax_bits8(xv[j]));
+        m = group_max_u32<64>(m);
+        if (lane == 0)
+            red[wave] = m;
+        __syncthreads();
+        m = max(max(red[0], red[1]), max(red[2], red[3]));
+        s = quant_scale(h2f((uint16_t)m), 127.0f);
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int c = tid + 256 * j;
+            if (c < nx) {
+                // k 8c .. 8c+7 -> (even k, odd k): the order of the low and
+                // high nibbles of the weight dword that covers them
+                const uint2 q = quant_chunk8(xv[j], s, r, 127.0f);
+                *reinterpret_cast<uint2 *>(xq_s + c * 8) =
+                    make_uint2(__builtin_amdgcn_perm(q.y, q.x, 0x06040200u),
+                               __builtin_amdgcn_perm(q.y, q.x, 0x07050301u));
+            }
+        }
+    } else {
+        // groups of GS / 8 consecutive threads share a group of the token
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) {
+            const int c = tid + 256 * j;
+            const uint32_t m = group_max_u32<GS / 8>(absmax_bits8(xv[j]));
+            const float sg = quant_scale(h2f((uint16_t)m), 127.0f);
+            const float r = 1.0f / sg;
+            if (c < nx) {
+                *reinterpret_cast<uint2 *>(xq_s + c * 8) = quant_chunk8(xv[j], sg, r, 127.0f);
+                if (tid % (GS / 8) == 0)
+                    sa_s[(c * 8) / GS] = sg;
+            }
+        }
+    }
+    __syncthreads();
+
+    // 4. per chunk: int32 dot product, summed over the group's lanes, folded
+    // by the group's first lane
+    float acc = 0.0f;
+    for (int base = 0;; base += LPR * CPL) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = base + lr + LPR * j;
+            int p = 0;
+            if (c < nch) {
+                const uint4 v = wv[j];
+                if constexpr (INT4) {
+                    const uint4 q0 = *reinterpret_cast<const uint4 *>(xq_s + c * 32);
+                    const uint4 q1 = *reinterpret_cast<const uint4 *>(xq_s + c * 32 + 16);
+                    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+                    const uint32_t qe[4] = {q0.x, q0.z, q1.x, q1.z}, qo[4] = {q0.y, q0.w, q1.y, q1.w};
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        p = __builtin_amdgcn_sdot4((int)((wd[d] << 4) & 0xf0f0f0f0u), (int)qe[d], p, false);
+                        p = __builtin_amdgcn_sdot4((int)(wd[d] & 0xf0f0f0f0u), (int)qo[d], p, false);
+                    }
+                } else {
+                    const uint4 q = *reinterpret_cast<const uint4 *>(xq_s + c * 16);
+                    p = __builtin_amdgcn_sdot4((int)v.x, (int)q.x, p, false);
+                    p = __builtin_amdgcn_sdot4((int)v.y, (int)q.y, p, false);
+                    p = __builtin_amdgcn_sdot4((int)v.z, (int)q.z, p, false);
+                    p = __builtin_amdgcn_sdot4((int)v.w, (int)q.w, p, false);
+                }
+            }
+            p = group_sum_i32<CPG>(p);              // every lane of the wave takes part
+            if (leader && c < nch) {
+                const float sc = INT4 ? swv[j] : sa_s[c / CPG] * swv[j];
+                acc = fmaf((float)p, sc, acc);
+            }
+        }
+        const int next = base + LPR * CPL;
+        if (next >= nch)
+            break;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = next + lr + LPR * j;
+            wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = next + lr + LPR * j;
+            swv[j] = (leader && c < nch) ? swr[c / CPG] : 0.0f;
+        }
+    }
+    acc = group_sum_f32<LPR>(acc);
+    if (lr == 0 && n < N)
+        y[n] = f2h(INT4 ? acc * (s * 0.0625f) : acc);
+}
+
+template <bool INT4, int GS, int LPR, int CPL, int XCH>
+void launch_group(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
+                  int K, hipStream_t st)
+{
+    constexpr int RPB = 256 / LPR;
+    const unsigned blocks = (unsigned)((N + RPB - 1) / RPB);
+    const size_t lds = (size_t)K + sizeof(float) * (INT4 ? 0 : K / GS);
+    hipLaunchKernelGGL((mv_group_kernel<INT4, GS, LPR, CPL, XCH>), dim3(blocks), dim3(256), lds,
+                       st, x, w, sw, y, N, K);
+}
+
+// 16 lanes per row (16 rows per workgroup, so the token's quantization is
+// shared by 16 rows at any K); chunks in flight per lane by the row's
+// 16-byte chunks (rows longer than 256 chunks take several passes); token
+// chunks per thread by K.
+template <bool INT4, int GS>
+void launch_group_k(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
+                    int K, hipStream_t st)
+{
+    const int nch = (INT4 ? K / 2 : K) / 16;
+    if (K <= 4096) {
+        if (nch <= 64)
+            launch_group<INT4, GS, 16, 4, 2>(x, w, sw, y, N, K, st);
+        else if (nch <= 128)
+            launch_group<INT4, GS, 16, 8, 2>(x, w, sw, y, N, K, st);
+        else
+            launch_group<INT4, GS, 16, 16, 2>(x, w, sw, y, N, K, st);
+    } else if (K <= 8192) {
+        launch_group<INT4, GS, 16, 16, 4>(x, w, sw, y, N, K, st);
+    } else if (K <= 16384) {
+        launch_group<INT4, GS, 16, 16, 8>(x, w, sw, y, N, K, st);
+    } else {
+        launch_group<INT4, GS, 16, 16, 16>(x, w, sw, y, N, K, st);
+    }
+}
+
 }  // namespace
 
 void launch_int8_mv(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, int N,
@@ -160,6 +378,15 @@ void launch_int8_mv(const uint16_t *x, const int8_t *w, const float *sw, uint16_
         launch_x<16, 16>(x, w, sw, y, N, K, xq_out, xs_out, st);
     else
         launch_x<64, 16>(x, w, sw, y, N, K, xq_out, xs_out, st);
+}
+
+void launch_mv_group(bool int4, int gs, const uint16_t *x, const uint8_t *w, const float *sw,
+                     uint16_t *y, int N, int K, hipStream_t st)
+{
+    if (int4)
+        (gs == 64 ? launch_group_k<true, 64> : launch_group_k<true, 128>)(x, w, sw, y, N, K, st);
+    else
+        (gs == 64 ? launch_group_k<false, 64> : launch_group_k<false, 128>)(x, w, sw, y, N, K, st);
 }
 
 }  // namespace w4a8

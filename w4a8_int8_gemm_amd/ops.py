@@ -151,12 +151,38 @@ def int8_mv(x, wq, w_scale, out=None, return_codes: bool = False):
     return (out, xq, xs) if return_codes else out
 
 
+def _mv_group(fn, x, w, w_scale, group_size: int, packed: bool, out):
+    if x.dim() == 2 and x.shape[0] == 1:
+        x = x.reshape(-1)
+    _need(x, torch.float16, "x", 1)
+    _need(w, torch.uint8 if packed else torch.int8, "w", 2)
+    _need(w_scale, torch.float32, "w_scale", 2)
+    K = x.shape[0]
+    N = w.shape[0]
+    if w.shape[1] * (2 if packed else 1) != K:
+        raise ValueError("weight shape does not match K")
+    out = _out(out, (N,), torch.float16, x, "out")
+    with torch.cuda.device(x.device):
+        check(getattr(lib(), fn)(_p(x), _p(w), _p(w_scale), group_size, _p(out), N, K, _st(x)))
+    return out
+
+
+def w8a8_mv_pg(x, wq, w_scale, group_size: int, out=None):
+    """Decode, per-group W8A8: x fp16 [K] -> y fp16 [N]; w_scale [N, K/gs]."""
+    return _mv_group("w8a8_mv_pg", x, wq, w_scale, group_size, False, out)
+
+
+def w4a8_mv(x, w4, w_scale, group_size: int, out=None):
+    """Decode, W4A8: x fp16 [K], packed w4 [N, K/2], w_scale [N, K/gs] -> y fp16 [N]."""
+    return _mv_group("w4a8_mv", x, w4, w_scale, group_size, True, out)
+
+
 def linear_workspace_size(mode, M: int, K: int, group_size: int = 0) -> int:
     return int(lib().linear_workspace_size(int(mode), M, K, group_size))
 
 
 def linear(mode, x, w, w_scale, group_size: int = 0, workspace=None, out=None):
-    """The whole layer: int8_mv when M == 1 in per-channel mode, else quantize + GEMM."""
+    """The whole layer: the mode's matrix-vector kernel when M == 1, else quantize + GEMM."""
     mode = Mode(mode)
     _need(x, torch.float16, "x", 2)
     packed = mode == Mode.W4A8
