@@ -7,6 +7,7 @@ on no branch or label between the write and the load.  This test compiles
 gemm.hip to device assembly and fails on any M0 access outside the copies'
 asm blocks and on any copy not preceded by an M0 write in its basic block."""
 import os
+import sys
 import re
 import subprocess
 
@@ -15,6 +16,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "w4a8_int8_gemm_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+sys.path.insert(0, ROOT)
+from w4a8_int8_gemm_amd.build import FLAGS  # noqa: E402  (plain list; imports nothing else)
 
 
 @pytest.fixture(scope="module")
@@ -22,9 +25,9 @@ def gemm_asm(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
     out = str(tmp_path_factory.mktemp("isa") / "gemm.s")
-    cmd = [HIPCC, "--offload-arch=gfx950", "--cuda-device-only", "-S", "-O3", "-std=c++17",
-           "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, "gemm.hip"), "-o", out]
+    # the library's own device flags, so the checked code is the shipped code
+    flags = [f for f in FLAGS if f != "-fPIC"]
+    cmd = [HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm.hip"), "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
     return open(out).read()
 

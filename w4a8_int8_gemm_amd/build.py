@@ -3,7 +3,8 @@
 Each translation unit is compiled by hipcc in parallel, then linked into one
 shared library next to this file.  Packed-fp32 instructions are disabled for
 all device code, and floating-point contraction is off: every fp32 operation
-rounds as written (explicit fmaf where a fused multiply-add is meant).
+rounds as written (explicit fmaf where a fused multiply-add is meant).  MFMA
+accumulators are allocated in ordinary VGPRs.
 """
 from __future__ import annotations
 
@@ -23,6 +24,9 @@ SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "mv.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the per-group folds read the int32 sums
+    # with plain VALU ops instead of first copying them out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -251,9 +251,14 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 
     __shared__ __attribute__((aligned(1024))) int8_t xs[3 * XBUF];
     __shared__ __attribute__((aligned(1024))) int8_t ws[3 * WBUF];
+    // Group scales have a ring of their own, one slot per stage: a group is
+    // folded after its last k-step, which for the last group of a stage comes
+    // after the barrier of its iteration, while a wave that is already past
+    // that barrier issues the scale copies of stages up to three ahead.
+    constexpr int SR = 5;                             // scale ring slots
     constexpr int SAL = T::fold_sa ? NG * BM : 1, SWL = T::fold_sw ? NG * BN : 1;
-    __shared__ __attribute__((aligned(16))) float sas[T::fold_sa ? 3 * SAL : 1];
-    __shared__ __attribute__((aligned(16))) float sws[T::fold_sw ? 3 * SWL : 1];
+    __shared__ __attribute__((aligned(16))) float sas[T::fold_sa ? SR * SAL : 1];
+    __shared__ __attribute__((aligned(16))) float sws[T::fold_sw ? SR * SWL : 1];
     __shared__ __attribute__((aligned(16))) float eps[EW > 0 ? EW * NW * 64 : 1];
 
     const int M = args.M, N = args.N, K = args.K;
@@ -329,6 +334,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         int s;         // stage within its tile
         int tile;      // tile within this workgroup's list
         int buf;       // LDS buffer (the unclamped stage index mod 3)
+        int sb;        // scale ring slot (the unclamped stage index mod SR)
         int m0, n0;    // tile origin
         v4i rx, rw;    // buffer resources of the tile's X rows and int8 W rows
     };
@@ -341,6 +347,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     };
     auto advance = [&](Src &c) __attribute__((always_inline)) {
         c.buf = c.buf == 2 ? 0 : c.buf + 1;
+        c.sb = c.sb == SR - 1 ? 0 : c.sb + 1;
         if (c.v + 1 < U) {                            // past the end: repeat the last stage
             ++c.v;
             if (++c.s == nstage) {
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                     const int gi = min(src.s * NG + g, G_ - 1);
                     if (e < NG * BM)
                         copy4_to_lds(args.sa + (int64_t)min(src.m0 + r, M - 1) * G_ + gi,
-                                     lds_addr(sas + buf * SAL + ins * 64));
+                                     lds_addr(sas + src.sb * SAL + ins * 64));
                 }
             }
         } else {
@@ -405,7 +412,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                     const int gi = min(src.s * NG + g, G_ - 1);
                     if (e < NG * BN)
                         copy4_to_lds(args.sw + (int64_t)min(src.n0 + r, N - 1) * G_ + gi,
-                                     lds_addr(sws + buf * SWL + ins * 64));
+                                     lds_addr(sws + src.sb * SWL + ins * 64));
                 }
             }
         }
@@ -535,6 +542,32 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     // r after MFMA r * FN * FM / (2 NR): all within the first half of the
     // step, so they have landed when the next step starts), and copies
     // [c0, c0 + n) of the stage `src` (copy p after MFMA (2p + 1) * FN * FM / (2n)).
+    // Fold (per-group modes): the group's int32 sums, rescaled by the group's
+    // scales, are added to the fp32 accumulators.  Chunk c = (m-block i, row
+    // quad q) covers elements 4q..4q+3 of blocks (j, i) for every j; its
+    // activation scales are read one chunk ahead.
+    constexpr int NCH = FM * 4;
+    auto fold_group = [&](int slot, int g) __attribute__((always_inline)) {
+        float fsw[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            fsw[j] = sws[slot * SWL + g * BN + wn * TN + j * 32 + out_n];
+        v4f fsa = {1.0f, 1.0f, 1.0f, 1.0f};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int i = c / 4, q = c % 4;
+            if constexpr (T::fold_sa)
+                fsa = *reinterpret_cast<const v4f *>(&sas[slot * SAL + g * BM + wm * TM + i * 32 + q * 8 + out_m]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sc = T::fold_sa ? fsa[r] * fsw[j] : fsw[j];
+                    accf[j][i][4 * q + r] = fmaf((float)acc[j][i][4 * q + r], sc, accf[j][i][4 * q + r]);
+                }
+        }
+    };
+
     auto mfma_step = [&](const Frag &F, auto RESTART, Frag &G, bool reads, int rbuf, int rt,
                          const Src &src, int sbuf, int c0, int n, auto KFULL)
                          __attribute__((always_inline)) {
@@ -585,30 +618,6 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 #pragma unroll
             for (int i = 0; i < FM; ++i)   // int4: exact, the sums are 16 * P
                 store_block_i32(P, acc[j][i], m0 + wm * TM + i * 32, n0 + wn * TN + j * 32, T::int4);
-    };
-
-    auto fold_group = [&](int buf, int g) __attribute__((always_inline)) {
-        float swv[FN];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            swv[j] = sws[buf * SWL + g * BN + wn * TN + j * 32 + out_n];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                v4f sav = {1.0f, 1.0f, 1.0f, 1.0f};
-                if constexpr (T::fold_sa)
-                    sav = *reinterpret_cast<const v4f *>(
-                        &sas[buf * SAL + g * BM + wm * TM + i * 32 + q * 8 + out_m]);
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float sc = T::fold_sa ? sav[r] * swv[j] : swv[j];
-                        accf[j][i][4 * q + r] =
-                            fmaf((float)acc[j][i][4 * q + r], sc, accf[j][i][4 * q + r]);
-                    }
-            }
     };
 
     // ---- the tile's outputs from the final sums
@@ -765,7 +774,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     auto main_loop = [&](auto KFULL) __attribute__((always_inline)) {
         constexpr bool kfull = decltype(KFULL)::value;   // K % 128 == 0: every k-step exists
         Src cp;                                       // stage 0, then 1, 2 (prologue)
-        cp.v = 0; cp.s = 0; cp.buf = 0;
+        cp.v = 0; cp.s = 0; cp.buf = 0; cp.sb = 0;
         set_tile(cp, 0);
         int cm0 = cp.m0, cn0 = cp.n0, ctile = 0;      // the tile being computed
         if constexpr (EW > 0)
@@ -789,6 +798,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         read_frag(f0, 0, 0);
 
         int b = 0, s = 0;                             // buffer and in-tile stage of iteration u
+        int sb = 0;                                   // scale ring slot of iteration u
         for (int u = 0; u < U; ++u) {
             const int b1 = b == 2 ? 0 : b + 1;
             const int ks0 = s * 4;
@@ -822,15 +832,13 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
                                   KFULL);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (T::pergroup) {      // close a group if one ends here
-                        const int ks = ks0 + t;
-                        if ((t + 1) % SPG == 0 || ks + 1 == nks) {
-                            const int gl = t / SPG;   // group slot within the stage
-                            if constexpr (T::partials)
-                                store_partials(cm0, cn0, s * NG + gl);
-                            else
-                                fold_group(b, gl);
-                        }
+                    // close a group where one ends (groups are whole runs of
+                    // k-steps: K % gs == 0)
+                    if constexpr (T::pergroup && (t + 1) % SPG == 0) {
+                        if constexpr (T::partials)
+                            store_partials(cm0, cn0, s * NG + t / SPG);
+                        else
+                            fold_group(sb, t / SPG);
                     }
                 } else {
                     // a K % 128 == 64 tail: the step does not exist, its copies
@@ -875,6 +883,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
             c2 = c3;
             advance(c3);
             b = b1;
+            sb = sb == SR - 1 ? 0 : sb + 1;
         }
         // no copy may still be writing LDS when the workgroup ends
         wait_vmcnt<0>();
@@ -936,6 +945,15 @@ void launch_mode(const GemmArgs &a, hipStream_t st)
         }
         if (t256x128 >= 512) {
             launch_cfg<256, 128, 2, 2, MODE, GS>(a, st);
+            return;
+        }
+    }
+    // per-group gs=64 with one set needs more than the 256 registers a wave
+    // has at two waves per SIMD; it stays at 128x128
+    if constexpr (pergroup && !(MODE == GemmMode::PG && GS == 64)) {
+        const int64_t t256x128p = (int64_t)((a.M + 255) / 256) * ((a.N + 127) / 128);
+        if (t256x128p >= 384) {            // two waves per SIMD: folds run beside MFMAs
+            launch_cfg<256, 128, 4, 2, MODE, GS>(a, st);
             return;
         }
     }
