@@ -48,8 +48,12 @@ def test_gemm_i32_and_pc(torch_gpu, oracle, M, N, K):
     assert stats["exact_frac"] > 0.99, stats
 
 
+# The last three reach the 256x128 two-waves-per-SIMD tiles (>= 384 tiles);
+# 1800x6100 is ragged in both M and N, and K = 448 leaves a 64-wide K tail
+# (gs = 64 only).
 PG_SHAPES = [(16, 512, 256), (3, 100, 384), (200, 300, 640), (257, 321, 512),
-             (70, 200, 320), (1024, 4096, 256), (2048, 8192, 256)]
+             (70, 200, 320), (1024, 4096, 256), (2048, 8192, 256), (1800, 6100, 384),
+             (1800, 6100, 448)]
 
 
 @pytest.mark.parametrize("gs", [64, 128])
