@@ -16,6 +16,7 @@ oracle timed on a bounded sample of rows of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --copy-probe      # plain copy kernel, for HBM counter scaling
+    python bench.py --kernel-sample   # three launches of each large GEMM kind, for --pmc runs
     python bench.py --suite [--steps K]   # timing table over every workload shape
 """
 from __future__ import annotations
@@ -58,6 +59,8 @@ def parse():
                     help="time every workload shape (a table, not the JSON line)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain copy of known size (HBM counter calibration)")
+    ap.add_argument("--kernel-sample", action="store_true",
+                    help="run each large GEMM kind three times (for rocprofv3 --pmc counter runs)")
     return ap.parse_args()
 
 
@@ -77,6 +80,47 @@ def traffic_from_profiles(per_launch_bytes_alg: float):
     if t.get("gemm_source_sha256_16") != gemm_source_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+def kernel_sample():
+    """Three launches of each large GEMM kind, nothing else timed or printed
+    on stdout: the per-channel headline, per-group gs=128 and gs=64 at
+    4096x14336x4096, and the W4A8 gate_up linear (4516x24576x4096).  Meant to
+    run under `rocprofv3 --pmc` (a few dispatches per kernel)."""
+    import torch
+
+    import synth
+    import w4a8_int8_gemm_amd as w
+
+    torch.cuda.set_device(0)
+    L = w.lib()
+    P = ctypes.c_void_p
+    sp = P(torch.cuda.current_stream().cuda_stream)
+
+    def ptr(t):
+        return P(t.data_ptr())
+
+    for mode, gs, M, N, K in [("pc", 0, 4096, 10240, 2560), ("pg", 128, 4096, 14336, 4096),
+                              ("pg", 64, 4096, 14336, 4096), ("w4a8", 128, 4516, 24576, 4096)]:
+        log(f"kernel sample: {mode} gs={gs} M={M} N={N} K={K}")
+        x = torch.from_numpy(synth.activations(M, K, seed=1)).cuda()
+        wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        if mode == "w4a8":
+            wq, sw = w.pack_weight_int4(wt, gs)
+        else:
+            wq, sw = w.quantize_weight_int8(wt, gs)
+        xq, xs = w.quantize_act(x, gs if mode == "pg" else 0)
+        for _ in range(3):
+            if mode == "pc":
+                w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y), M, N, K, sp))
+            elif mode == "pg":
+                w.check(L.w8a8_gemm_pg(ptr(xq), ptr(xs), ptr(wq), ptr(sw), gs, ptr(y), M, N, K, sp))
+            else:
+                w.check(L.w4a8_gemm(ptr(xq), ptr(xs), ptr(wq), ptr(sw), gs, ptr(y), M, N, K, sp))
+        torch.cuda.synchronize()
+        del x, wt, y, wq, sw, xq, xs
+        torch.cuda.empty_cache()
 
 
 def copy_probe():
@@ -263,6 +307,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.kernel_sample:
+        kernel_sample()
         return
     if args.suite:
         suite(args.steps)
