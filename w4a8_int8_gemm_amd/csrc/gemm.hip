@@ -36,7 +36,9 @@
 //    layout; the factor 16 is undone in the epilogue (exact).
 //  * Per-group modes restart the int32 accumulators for every group and fold
 //    them into fp32 accumulators with the group's scales, which are staged
-//    through LDS together with the tiles.
+//    through LDS together with the tiles (in a ring of their own).  Their
+//    large tiles run two waves per SIMD: the fold is VALU work that does not
+//    overlap the MFMAs of its own wave, only those of the other wave.
 //  * Workgroups are renumbered so that each XCD (one L2 each) works on a
 //    contiguous range of tiles, ordered in groups of `group_m` tile rows.
 #include <type_traits>
@@ -537,15 +539,11 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
             read_one(F, buf, t, r);
     };
 
-    // The MFMAs of one k-step (restarting the sums when RESTART) on F.
-    // Interleaved with them: the fragments of the next step into G (fragment
-    // r after MFMA r * FN * FM / (2 NR): all within the first half of the
-    // step, so they have landed when the next step starts), and copies
-    // [c0, c0 + n) of the stage `src` (copy p after MFMA (2p + 1) * FN * FM / (2n)).
     // Fold (per-group modes): the group's int32 sums, rescaled by the group's
     // scales, are added to the fp32 accumulators.  Chunk c = (m-block i, row
-    // quad q) covers elements 4q..4q+3 of blocks (j, i) for every j; its
-    // activation scales are read one chunk ahead.
+    // quad q) covers elements 4q..4q+3 of blocks (j, i) for every j and
+    // needs the four activation scales of those rows.  The group's scales
+    // are read from its stage's slot of the scale ring.
     constexpr int NCH = FM * 4;
     auto fold_group = [&](int slot, int g) __attribute__((always_inline)) {
         float fsw[FN];
@@ -568,6 +566,11 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         }
     };
 
+    // The MFMAs of one k-step (restarting the sums when RESTART) on F.
+    // Interleaved with them: the fragments of the next step into G (fragment
+    // r after MFMA r * FN * FM / (2 NR): all within the first half of the
+    // step, so they have landed when the next step starts), and copies
+    // [c0, c0 + n) of the stage `src` (copy p after MFMA (2p + 1) * FN * FM / (2n)).
     auto mfma_step = [&](const Frag &F, auto RESTART, Frag &G, bool reads, int rbuf, int rt,
                          const Src &src, int sbuf, int c0, int n, auto KFULL)
                          __attribute__((always_inline)) {
@@ -922,7 +925,9 @@ void launch_cfg(const GemmArgs &a, hipStream_t st)
 
 // Pick a tile shape: large tiles when the output is big, smaller ones when
 // too few tiles would leave compute units idle.  The per-group modes hold
-// fp32 accumulators next to the int32 ones and stay at 128x128 or below.
+// fp32 accumulators next to the int32 ones, so their large tile is 256x128
+// with eight 64x64 waves (two per SIMD, which lets one wave's fold run beside
+// the other's MFMAs) rather than four larger ones.
 template <GemmMode MODE, int GS>
 void launch_mode(const GemmArgs &a, hipStream_t st)
 {
@@ -951,8 +956,7 @@ void launch_mode(const GemmArgs &a, hipStream_t st)
     // per-group gs=64 with one set needs more than the 256 registers a wave
     // has at two waves per SIMD; it stays at 128x128
     if constexpr (pergroup && !(MODE == GemmMode::PG && GS == 64)) {
-        const int64_t t256x128p = (int64_t)((a.M + 255) / 256) * ((a.N + 127) / 128);
-        if (t256x128p >= 384) {            // two waves per SIMD: folds run beside MFMAs
+        if (t256x128 >= 384) {             // two waves per SIMD: folds run beside MFMAs
             launch_cfg<256, 128, 4, 2, MODE, GS>(a, st);
             return;
         }
