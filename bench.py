@@ -85,8 +85,13 @@ def traffic_from_profiles(per_launch_bytes_alg: float):
 def kernel_sample():
     """Three launches of each large GEMM kind, nothing else timed or printed
     on stdout: the per-channel headline, per-group gs=128 and gs=64 at
-    4096x14336x4096, and the W4A8 gate_up linear (4516x24576x4096).  Meant to
-    run under `rocprofv3 --pmc` (a few dispatches per kernel)."""
+    4096x14336x4096, and the W4A8 gate_up linear (4516x24576x4096); then the
+    HBM-bound kernels: quantize_act per token (4096x2560) and per group
+    (4096x4096, gs 128 and 64), and the decode matrix-vector kernels
+    (int8_mv 10240x2560, w8a8_mv_pg 14336x4096 gs=128, w4a8_mv 24576x4096),
+    each three times with a 1 GiB buffer written before every call so the
+    weights come from HBM.  Meant to run under `rocprofv3 --pmc` (a few
+    dispatches per kernel)."""
     import torch
 
     import synth
@@ -121,6 +126,39 @@ def kernel_sample():
         torch.cuda.synchronize()
         del x, wt, y, wq, sw, xq, xs
         torch.cuda.empty_cache()
+
+    for M, K, gs in [(4096, 2560, 0), (4096, 4096, 128), (4096, 4096, 64)]:
+        log(f"kernel sample: quantize_act M={M} K={K} gs={gs}")
+        x = torch.from_numpy(synth.activations(M, K, seed=1)).cuda()
+        for _ in range(3):
+            w.quantize_act(x, gs)
+        torch.cuda.synchronize()
+        del x
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for kind, gs, N, K in [("pc", 0, 10240, 2560), ("pg", 128, 14336, 4096),
+                           ("w4a8", 128, 24576, 4096)]:
+        log(f"kernel sample: decode {kind} gs={gs} N={N} K={K}")
+        x = torch.from_numpy(synth.activations(1, K, seed=1)).cuda()
+        wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
+        y = torch.empty((N,), dtype=torch.float16, device="cuda")
+        if kind == "w4a8":
+            wq, sw = w.pack_weight_int4(wt, gs)
+        else:
+            wq, sw = w.quantize_weight_int8(wt, gs)
+        del wt
+        for _ in range(3):
+            flush.fill_(1)
+            if kind == "pc":
+                w.check(L.int8_mv(ptr(x), ptr(wq), ptr(sw), ptr(y), N, K, None, None, sp))
+            elif kind == "pg":
+                w.check(L.w8a8_mv_pg(ptr(x), ptr(wq), ptr(sw), gs, ptr(y), N, K, sp))
+            else:
+                w.check(L.w4a8_mv(ptr(x), ptr(wq), ptr(sw), gs, ptr(y), N, K, sp))
+        torch.cuda.synchronize()
+        del x, y, wq, sw
+    del flush
+    torch.cuda.empty_cache()
 
 
 def copy_probe():
