@@ -175,10 +175,11 @@ def copy_probe():
 def suite(reps):
     """Per-workload kernel timings (not the JSON line): every shape of
     synth.WORKLOADS through its path, each kernel `reps` times back to back
-    between two events, through the C entry points.  The decode shape (M=1)
-    is timed warm (weights resident in the 256 MB Infinity Cache after the
-    first call) and cold (a 1 GiB buffer written between calls; run under
-    `rocprofv3 --kernel-trace` for those per-dispatch durations)."""
+    between two events, through the C entry points.  The decode shapes (M=1),
+    and quantize + GEMM of the per-channel M=128 and M=4096 shapes, are also
+    run cold (a 1 GiB buffer written before every call, so inputs come from
+    HBM rather than the 256 MB Infinity Cache); run under
+    `rocprofv3 --kernel-trace` for those per-dispatch durations."""
     import numpy as np
     import torch
 
@@ -248,6 +249,16 @@ def suite(reps):
                                                 M, N, K, sp))
             q()
             qus, gus = b2b(q), b2b(g)
+            if mode == "pc" and M in (128, 4096):
+                # cold: a 1 GiB buffer written before every quantize + GEMM
+                # pair (per-dispatch durations in the kernel trace)
+                flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+                for _ in range(reps):
+                    flush.fill_(1)
+                    q()
+                    g()
+                torch.cuda.synchronize()
+                del flush
             qbytes = 3 * M * K
             rows.append(f"{name:10s} M={M:5d} N={N:5d} K={K:5d}  quantize {qus:7.2f} us "
                         f"({qbytes / qus / 1e3:5.0f} GB/s) | gemm {gus:8.2f} us "
