@@ -309,6 +309,30 @@ def suite(reps):
         print(rows[-1], flush=True)
         del x, y, wq, sw, xq, xs
         torch.cuda.empty_cache()
+    # the pages' comparison: weight-only int8 (fp16 activations) against the
+    # W8A8 per-channel step (quantize + GEMM) at N=10240, K=2560
+    N, K = 10240, 2560
+    wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
+    wq, sw = w.quantize_weight_int8(wt, 0)
+    del wt
+    for M in (128, 1024, 4096, 8192):
+        x = torch.from_numpy(synth.activations(M, K, seed=1)).cuda()
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        xs = torch.empty((M, 1), dtype=torch.float32, device="cuda")
+        f16 = lambda: w.check(L.w8a16_gemm(ptr(x), ptr(wq), ptr(sw), ptr(y), M, N, K, sp))
+        step = lambda: (w.check(L.quantize_act(ptr(x), M, K, 0, ptr(xq), ptr(xs), sp)),
+                        w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y), M, N,
+                                               K, sp)))
+        tf, ts = b2b(f16), b2b(step)
+        ops = 2.0 * M * N * K
+        rows.append(f"w8a16_cmp  M={M:5d} N={N:5d} K={K:5d}  w8a16 {tf:8.2f} us {ops / tf / 1e6:7.1f} "
+                    f"TFLOPS ({100 * ops / tf / 1e6 / 2500.0:4.1f}% of fp16 peak) | w8a8 step "
+                    f"{ts:8.2f} us | w8a8 speed-up {tf / ts:5.2f}x")
+        print(rows[-1], flush=True)
+        del x, y, xq, xs
+    del wq, sw
+    torch.cuda.empty_cache()
     print("\n".join(rows), flush=True)
 
 

@@ -205,6 +205,22 @@ w4a8_status_t w4a8_gemm_partials(const int8_t *xq, const uint8_t *w4, int32_t gr
                                  int32_t *p, int64_t M, int64_t N, int64_t K,
                                  w4a8_stream_t stream);
 
+/* --------------------------------------------------------------------------
+ * Weight-only int8 comparison GEMM (W8A16): the baseline of the "cider"
+ * post's latency table (section on its performance results, which sets
+ * per-channel W8A8 against MLX's weight-only int8 product at N=10240,
+ * K=2560).  Activations stay fp16; the int8 codes are used as fp16 values
+ * (exact) on the fp16 matrix cores with fp32 accumulation:
+ *     y[m, n] = fp16( w_scale[n] * sum_k x[m,k] * wq[n,k] ).
+ * x fp16 [M, K], wq int8 [N, K] and w_scale fp32 [N] as produced by
+ * quantize_weight_int8 with group_size 0, y fp16 [M, N].  Requires
+ * K % 64 == 0 and M <= 65535 * 128; x, wq and y 16-byte aligned.  M == 0 or
+ * N == 0 returns W4A8_OK with no launch.  Not part of the W8A8 hot path: it
+ * exists to measure the W8A8 speed-up the pages report, on this GPU.
+ * ------------------------------------------------------------------------ */
+w4a8_status_t w8a16_gemm(const w4a8_f16 *x, const int8_t *wq, const float *w_scale,
+                         w4a8_f16 *y, int64_t M, int64_t N, int64_t K, w4a8_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,8 @@ def lib():
         L.oracle_f64_to_f16.argtypes = [ctypes.c_double]
         L.oracle_f64_to_f16.restype = ctypes.c_uint16
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_w8a16.argtypes = [_u16p, _i8p, _f32p, _i64, _i64, _i64, _u16p, _f64p]
+        L.oracle_w8a16.restype = None
         L.oracle_quantize_sym.argtypes = [_u16p, _i64, _i64, _i64, ctypes.c_int32, _i8p, _f32p]
         L.oracle_quantize_sym.restype = ctypes.c_int
         L.oracle_pack_int4.argtypes = [_i8p, _i64, _i64, _u8p]
@@ -272,3 +274,21 @@ def linear(mode: str, x: np.ndarray, w: np.ndarray, sw: np.ndarray, group_size: 
     if mode == "w4a8":
         return w4a8(x, w, sw, group_size)
     raise ValueError(mode)
+
+
+# ----------------------------------------------------------------------------- comparison path
+
+def w8a16(x: np.ndarray, wq: np.ndarray, sw: np.ndarray):
+    """Weight-only int8 product (the pages' W8A16 baseline): returns
+    ``(y fp16 [M, N], T float64 [M, N])`` with ``y = fp16(sw[n] * sum_k x w)``."""
+    x = np.ascontiguousarray(x, dtype=np.float16)
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    M, K = x.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K and sw.shape == (N,)
+    y = np.empty((M, N), dtype=np.float16)
+    t = np.empty((M, N), dtype=np.float64)
+    lib().oracle_w8a16(_p(x.view(np.uint16), _u16p), _p(wq, _i8p), _p(sw, _f32p), M, N, K,
+                       _p(y.view(np.uint16), _u16p), _p(t, _f64p))
+    return y, t

@@ -293,3 +293,30 @@ void oracle_epilogue_w4a8(const int32_t *P, const float *sa, const float *sw, in
                 T[m * N + n] = fabs((double)sa[m]) * mag;
         }
 }
+
+/* -------------------------------------------------------------------------
+ * Weight-only int8 product, the comparison baseline of the cider post's
+ * latency table (section on its performance results): activations stay
+ * fp16, weights are the int8 codes with per-channel scales:
+ *     Y[m, n] = fp16( sw[n] * sum_k x[m,k] * wq[n,k] ),
+ * the sum in binary64 (each product is exact: 11 x 8 significant bits), the
+ * scale applied once in binary64, one rounding to fp16.  T[m, n] = sw[n] *
+ * sum_k |x[m,k] * wq[n,k]| bounds the accumulation error of any fp32 order.
+ * ---------------------------------------------------------------------- */
+void oracle_w8a16(const uint16_t *X, const int8_t *W, const float *sw, int64_t M, int64_t N,
+                  int64_t K, uint16_t *Y, double *T)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0, a = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = oracle_f16_to_f64(X[m * K + k]) * (double)W[n * K + k];
+                s += p;
+                a += fabs(p);
+            }
+            Y[m * N + n] = oracle_f64_to_f16(s * (double)sw[n]);
+            T[m * N + n] = a * (double)sw[n];
+        }
+    }
+}

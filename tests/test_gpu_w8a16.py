@@ -1,0 +1,57 @@
+"""GPU parity of the weight-only int8 comparison GEMM (w8a16_gemm) against
+the oracle: fp16 outputs within 2e-3 relative (floor 2^-14) plus the fp32
+accumulation bound gamma_K * T, ragged edges and the pages' N=10240, K=2560
+shape (sampled rows at M=4096)."""
+import numpy as np
+import pytest
+
+import synth
+from tests.parity_util import assert_fp16_close, dev, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    return require_gpu()
+
+
+SHAPES = [(16, 512, 256), (3, 100, 384), (257, 321, 512), (200, 302, 640), (130, 1000, 64),
+          (1024, 4096, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_w8a16_small(torch_gpu, oracle, M, N, K):
+    import w4a8_int8_gemm_amd as w
+    print(f"w8a16 M={M} N={N} K={K}", flush=True)
+    x = synth.activations(M, K, seed=M + N)
+    wq, sw = oracle.quantize_weight_int8(synth.weights(N, K, seed=K), 0)
+    y_ref, t_ref = oracle.w8a16(x, wq, sw)
+    y = w.w8a16_gemm(dev(x), dev(wq), dev(sw))
+    stats = assert_fp16_close(host(y), y_ref, t_ref, K - 2, what="w8a16 y")
+    assert stats["exact_frac"] > 0.9, stats
+
+
+def test_w8a16_pages_shape_sampled(torch_gpu, oracle):
+    import w4a8_int8_gemm_amd as w
+    M, N, K = 4096, 10240, 2560
+    print(f"w8a16 M={M} N={N} K={K} (sampled rows)", flush=True)
+    x = synth.activations(M, K, seed=0)
+    wq, sw = oracle.quantize_weight_int8(synth.weights(N, K, seed=0), 0)
+    y = host(w.w8a16_gemm(dev(x), dev(wq), dev(sw)))
+    rows = synth.sample_indices(M, 24, seed=7, salt=3)
+    y_ref, t_ref = oracle.w8a16(x[rows], wq, sw)
+    stats = assert_fp16_close(y[rows], y_ref, t_ref, K - 2, what="w8a16 y (sampled rows)")
+    assert stats["exact_frac"] > 0.9, stats
+
+
+def test_w8a16_empty_and_bad_args(torch_gpu):
+    import torch
+    import w4a8_int8_gemm_amd as w
+    x = torch.zeros((0, 64), dtype=torch.float16, device="cuda")
+    wq = torch.zeros((8, 64), dtype=torch.int8, device="cuda")
+    sw = torch.ones(8, dtype=torch.float32, device="cuda")
+    assert w.w8a16_gemm(x, wq, sw).shape == (0, 8)
+    with pytest.raises(Exception):
+        w.w8a16_gemm(torch.zeros((4, 40), dtype=torch.float16, device="cuda"),
+                     torch.zeros((8, 40), dtype=torch.int8, device="cuda"), sw)

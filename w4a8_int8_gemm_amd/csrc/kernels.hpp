@@ -46,4 +46,9 @@ void launch_int8_mv(const uint16_t *x, const int8_t *w, const float *sw, uint16_
 void launch_mv_group(bool int4, int gs, const uint16_t *x, const uint8_t *w, const float *sw,
                      uint16_t *y, int N, int K, hipStream_t st);
 
+// Weight-only int8 comparison GEMM: y = fp16(w_scale[n] * sum_k x[m,k] wq[n,k])
+// with fp16 activations on the fp16 matrix cores (K % 64 == 0).
+void launch_w8a16(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, int M, int N,
+                  int K, hipStream_t st);
+
 }  // namespace w4a8

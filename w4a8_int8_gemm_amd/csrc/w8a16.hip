@@ -1,0 +1,179 @@
+// Weight-only int8 GEMM (W8A16), the comparison path of the "cider" post's
+// latency table (section on its performance results: per-channel W8A8
+// against MLX's weight-only int8 product at N=10240, K=2560).  Activations
+// stay fp16; the int8 weight codes are turned into fp16 (exact: |code| <= 128)
+// and multiplied on the fp16 matrix cores with fp32 accumulation:
+//     y[m, n] = fp16( w_scale[n] * sum_k x[m,k] * wq[n,k] ).
+//
+// Design (a plain comparison kernel, not tuned like the int8 paths):
+//  * 128 x 128 output tiles, four waves of 64 x 64, v_mfma_f32_32x32x16_f16
+//    with the weights as the first operand, so a lane holds one output row m
+//    and runs of four consecutive columns n (8-byte fp16 stores).
+//  * K advances 64 at a time through two LDS buffers; both operands sit in
+//    LDS as fp16 rows of 128 bytes with the 16-byte chunks XOR-swizzled per
+//    row (conflict-free 16-byte fragment reads).  The next stage's global
+//    loads are in flight while the current stage is multiplied; the weights
+//    are converted to fp16 when they are written to LDS.
+#include "kernels.hpp"
+
+namespace w4a8 {
+
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f16x __attribute__((ext_vector_type(16)));
+
+constexpr int TB = 128;          // tile rows (m) and columns (n)
+constexpr int KS = 64;           // k per stage: 128 bytes of fp16 per row
+
+// Physical 16-byte chunk of logical chunk c (0..7) in a 128-byte LDS row r:
+// sixteen consecutive rows read at one logical chunk hit distinct banks.
+__device__ __forceinline__ int swz16(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+// Four signed bytes to four fp16 values, exactly: byte b + 128 is placed
+// under the exponent byte 0x64 (fp16 1024 + (b + 128)), then 1152 is
+// subtracted in fp16 (exact, the result is the integer b).
+__device__ __forceinline__ uint2 int8x4_to_half4(uint32_t v)
+{
+    const uint32_t u = v ^ 0x80808080u;
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+    const h2 k = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const h2 a = __builtin_bit_cast(h2, lo) - k;
+    const h2 b = __builtin_bit_cast(h2, hi) - k;
+    return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
+__global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t *__restrict__ x,
+                                                    const int8_t *__restrict__ w,
+                                                    const float *__restrict__ sw,
+                                                    uint16_t *__restrict__ y, int M, int N, int K)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][TB * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t ws[2][TB * 128];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;          // 64 x 64 wave tile (n, m)
+    const int n0 = blockIdx.x * TB, m0 = blockIdx.y * TB;
+    const int nst = K / KS;
+
+    // global loads of one stage: X 1024 chunks of 16 bytes (4 per thread),
+    // W 512 chunks of 16 int8 (2 per thread); rows past the end read zeros
+    uint4 xr[4], wr[2];
+    auto load = [&](int s) __attribute__((always_inline)) {
+        const int64_t k0 = (int64_t)s * KS;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int c = tid + 256 * p, r = c >> 3, ch = c & 7;
+            const int m = m0 + r;
+            xr[p] = m < M ? *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k0 + ch * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int c = tid + 256 * p, r = c >> 2, ch = c & 3;
+            const int n = n0 + r;
+            wr[p] = n < N ? *reinterpret_cast<const uint4 *>(w + (int64_t)n * K + k0 + ch * 16)
+                          : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int c = tid + 256 * p, r = c >> 3, ch = c & 7;
+            *reinterpret_cast<uint4 *>(&xs[buf][r * 128 + swz16(r, ch) * 16]) = xr[p];
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int c = tid + 256 * p, r = c >> 2, ch = c & 3;   // 16 codes -> fp16 chunks 2ch, 2ch+1
+            const uint2 a = int8x4_to_half4(wr[p].x), b = int8x4_to_half4(wr[p].y);
+            const uint2 d = int8x4_to_half4(wr[p].z), e = int8x4_to_half4(wr[p].w);
+            *reinterpret_cast<uint4 *>(&ws[buf][r * 128 + swz16(r, 2 * ch) * 16]) =
+                make_uint4(a.x, a.y, b.x, b.y);
+            *reinterpret_cast<uint4 *>(&ws[buf][r * 128 + swz16(r, 2 * ch + 1) * 16]) =
+                make_uint4(d.x, d.y, e.x, e.y);
+        }
+    };
+
+    f16x acc[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            acc[j][i] = f16x{};
+
+    // fragment of k-step t (16 k): row base + lane % 32, logical chunk
+    // 2t + lane / 32 (eight fp16 values)
+    const int lr = lane & 31, lh = lane >> 5;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nst)
+            load(s + 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            h8 a[2], b[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = wn * 64 + j * 32 + lr;
+                a[j] = *reinterpret_cast<const h8 *>(&ws[buf][r * 128 + swz16(r, 2 * t + lh) * 16]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = wm * 64 + i * 32 + lr;
+                b[i] = *reinterpret_cast<const h8 *>(&xs[buf][r * 128 + swz16(r, 2 * t + lh) * 16]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b[i], acc[j][i], 0, 0, 0);
+        }
+        if (s + 1 < nst) {
+            store(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // epilogue: lane holds row m of block (j, i) and columns
+    // nb + 8g + 4 lh + 0..3 in elements 4g..4g+3
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wm * 64 + i * 32 + lr;
+        if (m >= M)
+            continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int nb = n0 + wn * 64 + j * 32;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = nb + 8 * g + 4 * lh;
+                if (vec && n + 3 < N) {
+                    const uint32_t p0 = pack_h2(acc[j][i][4 * g] * sw[n], acc[j][i][4 * g + 1] * sw[n + 1]);
+                    const uint32_t p1 =
+                        pack_h2(acc[j][i][4 * g + 2] * sw[n + 2], acc[j][i][4 * g + 3] * sw[n + 3]);
+                    *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) = make_uint2(p0, p1);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            y[(int64_t)m * N + n + r] = f2h(acc[j][i][4 * g + r] * sw[n + r]);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+void launch_w8a16(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, int M, int N,
+                  int K, hipStream_t st)
+{
+    const dim3 grid((unsigned)((N + TB - 1) / TB), (unsigned)((M + TB - 1) / TB));
+    hipLaunchKernelGGL(w8a16_kernel, grid, dim3(256), 0, st, x, w, sw, y, M, N, K);
+}
+
+}  // namespace w4a8

@@ -226,3 +226,19 @@ def w4a8_gemm_partials(xq, w4, group_size: int, out=None):
     with torch.cuda.device(xq.device):
         check(lib().w4a8_gemm_partials(_p(xq), _p(w4), group_size, _p(out), M, N, K, _st(xq)))
     return out
+
+
+def w8a16_gemm(x, wq, w_scale, out=None):
+    """Weight-only int8 comparison GEMM: y fp16 [M, N] = w_scale[n] * (x . wq^T),
+    x fp16 [M, K] (not quantized), wq int8 [N, K], w_scale fp32 [N]."""
+    _need(x, torch.float16, "x", 2)
+    _need(wq, torch.int8, "wq", 2)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError(f"weight shape {tuple(wq.shape)} does not match K={K}")
+    out = _out(out, (M, N), torch.float16, x, "out")
+    with torch.cuda.device(x.device):
+        check(lib().w8a16_gemm(_p(x), _p(wq), _p(w_scale), _p(out), M, N, K, _st(x)))
+    return out
