@@ -944,12 +944,22 @@ void launch_mode(const GemmArgs &a, hipStream_t st)
         return;
     }
     if constexpr (!pergroup) {
-        if (t256x160 >= 512 && a.N % 160 == 0) {
-            launch_cfg<256, 160, 4, 1, MODE, GS>(a, st);
-            return;
-        }
-        if (t256x128 >= 512) {
-            launch_cfg<256, 128, 2, 2, MODE, GS>(a, st);
+        // Large outputs: the cheapest of the three big tiles by (rounds of
+        // tiles over the compute units) x (tile area / its measured relative
+        // rate: 256x160 1, 256x128 0.9, 128x128 0.85), so that a last round
+        // left mostly empty counts against a tile shape.
+        if (t128x128 >= 256) {
+            const int64_t cu = a.num_cu > 0 ? a.num_cu : 1;
+            auto rounds = [&](int64_t t) { return (double)((t + cu - 1) / cu); };
+            const double c160 = a.N % 160 == 0 ? rounds(t256x160) * (256.0 * 160.0) : 1e300;
+            const double c256 = rounds(t256x128) * (256.0 * 128.0 / 0.9);
+            const double c128 = rounds(t128x128) * (128.0 * 128.0 / 0.85);
+            if (c160 <= c256 && c160 <= c128)
+                launch_cfg<256, 160, 4, 1, MODE, GS>(a, st);
+            else if (c256 <= c128)
+                launch_cfg<256, 128, 2, 2, MODE, GS>(a, st);
+            else
+                launch_cfg<128, 128, 2, 2, MODE, GS>(a, st);
             return;
         }
     }
