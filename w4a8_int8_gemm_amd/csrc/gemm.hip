@@ -963,11 +963,20 @@ void launch_mode(const GemmArgs &a, hipStream_t st)
             return;
         }
     }
-    // per-group gs=64 with one set needs more than the 256 registers a wave
-    // has at two waves per SIMD; it stays at 128x128
+    // per-group gs=64 at 256x128 needs more than the 256 registers a wave
+    // has at two waves per SIMD (it spills); it takes 128x128 below
     if constexpr (pergroup && !(MODE == GemmMode::PG && GS == 64)) {
         if (t256x128 >= 384) {             // two waves per SIMD: folds run beside MFMAs
             launch_cfg<256, 128, 4, 2, MODE, GS>(a, st);
+            return;
+        }
+    }
+    // per-group gs=64 is bound by its fold (VALU): eight 64x32 waves (two per
+    // SIMD, few registers) overlap one wave's fold with another's MFMAs; the
+    // extra LDS reads of the narrower waves cost nothing at its MFMA rate
+    if constexpr (MODE == GemmMode::PG && GS == 64) {
+        if (t128x128 >= 256) {
+            launch_cfg<128, 128, 2, 4, MODE, GS>(a, st);
             return;
         }
     }
