@@ -19,15 +19,18 @@ def torch_gpu():
     return require_gpu()
 
 
-# (M, N, K): covers 64x64 (M<=64), 128x64, 128x128, 256x128, 256x160 selections
+# (M, N, K): covers the 32x128, 64x128, 128x128, 256x128 and 256x160 selections
 PC_SHAPES = [
     (16, 512, 256), (1, 96, 64), (3, 100, 192), (64, 64, 64),
     (65, 130, 320), (200, 300, 192), (257, 321, 256),
     (1024, 4096, 128), (2048, 8192, 128), (2048, 10240, 128), (1500, 10240, 192),
-    # 256x128 tiles (N not a multiple of 160) with ragged M and N: whole
-    # stages only, rows not a multiple of 16 bytes (scalar stores), few
-    # stages per tile, a K tail
+    # ragged M and N (N not a multiple of 160), rows not a multiple of 16
+    # bytes (scalar stores), few stages per tile, a K tail: 128x128 and
+    # 256x128 tiles as the tile-cost model picks them
     (2000, 8200, 1024), (1800, 8196, 1280), (2048, 8192, 512), (2000, 8200, 320),
+    (1500, 8196, 320), (1500, 8200, 1280),
+    # 256x160 tiles, one round over the CUs, ragged M
+    (1000, 10240, 256),
 ]
 
 
