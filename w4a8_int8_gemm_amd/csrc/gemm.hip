@@ -8,7 +8,8 @@
 // "입도: Per-Tensor vs. Per-Channel vs. Per-Group").  INT4 weights are
 // unpacked to INT8 before the INT8 matmul ("cider" post, modes table).
 //
-// Design (CDNA4, wave64, one wave per SIMD for the large tiles):
+// Design (CDNA4, wave64; the per-channel large tiles run one wave per SIMD,
+// the per-group ones two):
 //  * One workgroup computes BM x BN tiles of Y (m x n) with WM x WN waves.
 //    Both operands are K-contiguous.  v_mfma_i32_32x32x32_i8 multiplies two
 //    32 x 32-k fragments (16 bytes per lane each); a lane of its result holds
