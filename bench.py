@@ -314,6 +314,7 @@ def suite(reps):
     N, K = 10240, 2560
     wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
     wq, sw = w.quantize_weight_int8(wt, 0)
+    w4, s4 = w.pack_weight_int4(wt, 128)
     del wt
     for M in (128, 1024, 4096, 8192):
         x = torch.from_numpy(synth.activations(M, K, seed=1)).cuda()
@@ -324,14 +325,16 @@ def suite(reps):
         step = lambda: (w.check(L.quantize_act(ptr(x), M, K, 0, ptr(xq), ptr(xs), sp)),
                         w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y), M, N,
                                                K, sp)))
-        tf, ts = b2b(f16), b2b(step)
+        f4 = lambda: w.check(L.w4a16_gemm(ptr(x), ptr(w4), ptr(s4), 128, ptr(y), M, N, K, sp))
+        tf, t4, ts = b2b(f16), b2b(f4), b2b(step)
         ops = 2.0 * M * N * K
         rows.append(f"w8a16_cmp  M={M:5d} N={N:5d} K={K:5d}  w8a16 {tf:8.2f} us {ops / tf / 1e6:7.1f} "
-                    f"TFLOPS ({100 * ops / tf / 1e6 / 2500.0:4.1f}% of fp16 peak) | w8a8 step "
-                    f"{ts:8.2f} us | w8a8 speed-up {tf / ts:5.2f}x")
+                    f"TFLOPS ({100 * ops / tf / 1e6 / 2500.0:4.1f}% of fp16 peak) | w4a16 gs=128 "
+                    f"{t4:8.2f} us | w8a8 step {ts:8.2f} us | w8a8 speed-up {tf / ts:5.2f}x over "
+                    f"w8a16, {t4 / ts:5.2f}x over w4a16")
         print(rows[-1], flush=True)
         del x, y, xq, xs
-    del wq, sw
+    del wq, sw, w4, s4
     torch.cuda.empty_cache()
     print("\n".join(rows), flush=True)
 

@@ -221,6 +221,18 @@ w4a8_status_t w4a8_gemm_partials(const int8_t *xq, const uint8_t *w4, int32_t gr
 w4a8_status_t w8a16_gemm(const w4a8_f16 *x, const int8_t *wq, const float *w_scale,
                          w4a8_f16 *y, int64_t M, int64_t N, int64_t K, w4a8_stream_t stream);
 
+/* Weight-only int4 comparison GEMM (W4A16), the latency table's other
+ * baseline (MLX's weight-only int4 product).  Each weight is dequantized to
+ * fp16 with its group's scale before the fp16 product:
+ *     y[m, n] = fp16( sum_k x[m,k] * fp16(fl32(code[n,k] * w_scale[n,g])) ),
+ * fp32 accumulation.  x fp16 [M, K]; w4 uint8 [N, K/2] and w_scale fp32
+ * [N, K/group_size] as produced by pack_weight_int4; group_size 64 or 128;
+ * K % 64 == 0 and K % group_size == 0; M <= 65535 * 128.  Same conventions
+ * as w8a16_gemm. */
+w4a8_status_t w4a16_gemm(const w4a8_f16 *x, const uint8_t *w4, const float *w_scale,
+                         int32_t group_size, w4a8_f16 *y, int64_t M, int64_t N, int64_t K,
+                         w4a8_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

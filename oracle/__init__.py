@@ -56,6 +56,8 @@ def lib():
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_w8a16.argtypes = [_u16p, _i8p, _f32p, _i64, _i64, _i64, _u16p, _f64p]
         L.oracle_w8a16.restype = None
+        L.oracle_w4a16.argtypes = [_u16p, _i8p, _f32p, _i64, _i64, _i64, _i64, _u16p, _f64p]
+        L.oracle_w4a16.restype = None
         L.oracle_quantize_sym.argtypes = [_u16p, _i64, _i64, _i64, ctypes.c_int32, _i8p, _f32p]
         L.oracle_quantize_sym.restype = ctypes.c_int
         L.oracle_pack_int4.argtypes = [_i8p, _i64, _i64, _u8p]
@@ -291,4 +293,21 @@ def w8a16(x: np.ndarray, wq: np.ndarray, sw: np.ndarray):
     t = np.empty((M, N), dtype=np.float64)
     lib().oracle_w8a16(_p(x.view(np.uint16), _u16p), _p(wq, _i8p), _p(sw, _f32p), M, N, K,
                        _p(y.view(np.uint16), _u16p), _p(t, _f64p))
+    return y, t
+
+
+def w4a16(x: np.ndarray, w4: np.ndarray, sw: np.ndarray, group_size: int):
+    """Weight-only int4 product (the pages' W4A16 baseline): each code is
+    dequantized to fp16(fl32(code * sw[n, g])); returns ``(y fp16 [M, N],
+    T float64 [M, N])`` with ``y = fp16(sum_k x * w)``."""
+    x = np.ascontiguousarray(x, dtype=np.float16)
+    M, K = x.shape
+    codes = np.ascontiguousarray(unpack_int4(w4, K), dtype=np.int8)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    N = codes.shape[0]
+    assert sw.shape == (N, K // group_size)
+    y = np.empty((M, N), dtype=np.float16)
+    t = np.empty((M, N), dtype=np.float64)
+    lib().oracle_w4a16(_p(x.view(np.uint16), _u16p), _p(codes, _i8p), _p(sw, _f32p), M, N, K,
+                       group_size, _p(y.view(np.uint16), _u16p), _p(t, _f64p))
     return y, t

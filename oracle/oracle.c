@@ -320,3 +320,38 @@ void oracle_w8a16(const uint16_t *X, const int8_t *W, const float *sw, int64_t M
         }
     }
 }
+
+/* Weight-only int4 product, the latency table's other baseline: each int4
+ * code (unpacked, [N, K]) is dequantized with its group's scale to fp16 as
+ * fp16(fl32(code * sw[n, k / gs])) -- an fp32 multiply, then one rounding to
+ * fp16 -- and Y[m, n] = fp16( sum_k x[m,k] * w[n,k] ), the sum in binary64
+ * (each product of two fp16 values is exact), rounded once.  T[m, n] =
+ * sum_k |x[m,k] * w[n,k]|. */
+void oracle_w4a16(const uint16_t *X, const int8_t *codes, const float *sw, int64_t M, int64_t N,
+                  int64_t K, int64_t gs, uint16_t *Y, double *T)
+{
+    const int64_t G = K / gs;
+    double *Wd = (double *)malloc((size_t)(N * K) * sizeof(double));
+    if (!Wd)
+        return;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const float p = (float)codes[n * K + k] * sw[n * G + k / gs];
+            Wd[n * K + k] = oracle_f16_to_f64(oracle_f64_to_f16((double)p));
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0, a = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = oracle_f16_to_f64(X[m * K + k]) * Wd[n * K + k];
+                s += p;
+                a += fabs(p);
+            }
+            Y[m * N + n] = oracle_f64_to_f16(s);
+            T[m * N + n] = a;
+        }
+    }
+    free(Wd);
+}

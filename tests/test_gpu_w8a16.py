@@ -55,3 +55,31 @@ def test_w8a16_empty_and_bad_args(torch_gpu):
     with pytest.raises(Exception):
         w.w8a16_gemm(torch.zeros((4, 40), dtype=torch.float16, device="cuda"),
                      torch.zeros((8, 40), dtype=torch.int8, device="cuda"), sw)
+
+
+@pytest.mark.parametrize("gs", [64, 128])
+@pytest.mark.parametrize("M,N,K", [(16, 512, 256), (3, 100, 384), (257, 321, 512), (200, 302, 640),
+                                   (1024, 4096, 256)])
+def test_w4a16_small(torch_gpu, oracle, M, N, K, gs):
+    import w4a8_int8_gemm_amd as w
+    if K % gs:
+        pytest.skip("K not a multiple of gs")
+    print(f"w4a16 M={M} N={N} K={K} gs={gs}", flush=True)
+    x = synth.activations(M, K, seed=M + N)
+    w4, s4 = oracle.pack_weight_int4(synth.weights(N, K, seed=K), gs)
+    y_ref, t_ref = oracle.w4a16(x, w4, s4, gs)
+    y = w.w4a16_gemm(dev(x), dev(w4), dev(s4), gs)
+    stats = assert_fp16_close(host(y), y_ref, t_ref, K - 2, what="w4a16 y")
+    assert stats["exact_frac"] > 0.9, stats
+
+
+def test_w4a16_every_nibble(torch_gpu, oracle):
+    """Packed bytes covering every nibble, including 0x8 (code -8)."""
+    import w4a8_int8_gemm_amd as w
+    M, N, K, gs = 64, 256, 256, 128
+    x = synth.activations(M, K, seed=9)
+    w4 = synth.packed_int4(N, K, 9, 1)
+    s4 = synth.scales(N, K // gs, 9, 1, 0.3)
+    y_ref, t_ref = oracle.w4a16(x, w4, s4, gs)
+    y = w.w4a16_gemm(dev(x), dev(w4), dev(s4), gs)
+    assert_fp16_close(host(y), y_ref, t_ref, K - 2, what="w4a16 y (every nibble)")

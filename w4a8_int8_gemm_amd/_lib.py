@@ -38,6 +38,7 @@ _SIGNATURES = {
     "w8a8_gemm_pg_partials": [_vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp],
     "w4a8_gemm_partials": [_vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp],
     "w8a16_gemm": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
+    "w4a16_gemm": [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp],
 }
 _RESTYPES = {
     "w4a8_is_available": ctypes.c_int,

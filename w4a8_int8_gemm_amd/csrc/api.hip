@@ -488,3 +488,32 @@ w4a8_status_t w8a16_gemm(const w4a8_f16 *x, const int8_t *wq, const float *w_sca
                  reinterpret_cast<uint16_t *>(y), (int)M, (int)N, (int)K, (hipStream_t)stream);
     return check_launch(fn);
 }
+
+w4a8_status_t w4a16_gemm(const w4a8_f16 *x, const uint8_t *w4, const float *w_scale,
+                         int32_t group_size, w4a8_f16 *y, int64_t M, int64_t N, int64_t K,
+                         w4a8_stream_t stream)
+{
+    const char *fn = "w4a16_gemm";
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return fail(W4A8_ERR_INVALID_ARG, "%s: sizes out of range (M=%lld N=%lld K=%lld)", fn,
+                    (long long)M, (long long)N, (long long)K);
+    if (!(group_size == 64 || group_size == 128))
+        return fail(W4A8_ERR_SHAPE, "%s: group_size=%d must be 64 or 128", fn, (int)group_size);
+    if (K == 0 || K % 64 != 0 || K % group_size != 0)
+        return fail(W4A8_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 64 and of "
+                    "group_size", fn, (long long)K);
+    if ((M + 127) / 128 > 65535)
+        return fail(W4A8_ERR_SHAPE, "%s: M=%lld exceeds 65535 * 128 rows", fn, (long long)M);
+    if (M == 0 || N == 0)
+        return ok();
+    if (!x || !w4 || !w_scale || !y)
+        return fail(W4A8_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned16(x) || !aligned16(w4) || !aligned16(y) || !aligned4(w_scale))
+        return fail(W4A8_ERR_ALIGNMENT, "%s: tensors must be 16-byte aligned", fn);
+    w4a8_status_t st = check_device();
+    if (st != W4A8_OK)
+        return st;
+    launch_w4a16(reinterpret_cast<const uint16_t *>(x), w4, w_scale, (int)group_size,
+                 reinterpret_cast<uint16_t *>(y), (int)M, (int)N, (int)K, (hipStream_t)stream);
+    return check_launch(fn);
+}

@@ -50,5 +50,9 @@ void launch_mv_group(bool int4, int gs, const uint16_t *x, const uint8_t *w, con
 // with fp16 activations on the fp16 matrix cores (K % 64 == 0).
 void launch_w8a16(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, int M, int N,
                   int K, hipStream_t st);
+// Weight-only int4 comparison GEMM: y = fp16(sum_k x[m,k] fp16(fl32(code[n,k]
+// w_scale[n,g]))) with packed int4 weights [N, K/2] (K % 64 == 0, K % gs == 0).
+void launch_w4a16(const uint16_t *x, const uint8_t *w4, const float *sw, int gs, uint16_t *y, int M,
+                  int N, int K, hipStream_t st);
 
 }  // namespace w4a8

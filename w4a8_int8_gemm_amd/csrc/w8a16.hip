@@ -1,9 +1,13 @@
-// Weight-only int8 GEMM (W8A16), the comparison path of the "cider" post's
-// latency table (section on its performance results: per-channel W8A8
-// against MLX's weight-only int8 product at N=10240, K=2560).  Activations
-// stay fp16; the int8 weight codes are turned into fp16 (exact: |code| <= 128)
-// and multiplied on the fp16 matrix cores with fp32 accumulation:
-//     y[m, n] = fp16( w_scale[n] * sum_k x[m,k] * wq[n,k] ).
+// Weight-only GEMMs (W8A16, W4A16), the comparison paths of the "cider"
+// post's latency table (section on its performance results: per-channel
+// W8A8 against MLX's weight-only int8 and int4 products at N=10240,
+// K=2560).  Activations stay fp16 and are multiplied on the fp16 matrix
+// cores with fp32 accumulation:
+//     W8A16: y[m, n] = fp16( w_scale[n] * sum_k x[m,k] * wq[n,k] ),
+//            the int8 codes turned into fp16 exactly (|code| <= 128);
+//     W4A16: y[m, n] = fp16( sum_k x[m,k] * fp16(fl32(code[n,k] * w_scale[n,g])) ),
+//            each int4 code dequantized with its group's scale to fp16
+//            before the product (weights packed as for w4a8_gemm).
 //
 // Design (a plain comparison kernel, not tuned like the int8 paths):
 //  * 128 x 128 output tiles, four waves of 64 x 64, v_mfma_f32_32x32x16_f16
@@ -45,11 +49,35 @@ __device__ __forceinline__ uint2 int8x4_to_half4(uint32_t v)
     return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
-__global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t *__restrict__ x,
-                                                    const int8_t *__restrict__ w,
-                                                    const float *__restrict__ sw,
-                                                    uint16_t *__restrict__ y, int M, int N, int K)
+// Eight packed int4 codes (one dword, low nibble = even k, two's-complement
+// nibbles) dequantized with scale s to fp16, in k order: a nibble XOR 8 is
+// u = code + 8, and fma(u, s, -8 s) rounds the exact code * s once, i.e.
+// gives fl32(code * s); then fp16.
+__device__ __forceinline__ uint4 int4x8_dequant(uint32_t v, float s)
 {
+    const uint32_t lo = (v & 0x0f0f0f0fu) ^ 0x08080808u;          // k = 0, 2, 4, 6
+    const uint32_t hi = ((v >> 4) & 0x0f0f0f0fu) ^ 0x08080808u;   // k = 1, 3, 5, 7
+    const float b = -8.0f * s;                        // exact (power of two)
+    float d[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        d[2 * i] = fmaf((float)((lo >> (8 * i)) & 0xffu), s, b);
+        d[2 * i + 1] = fmaf((float)((hi >> (8 * i)) & 0xffu), s, b);
+    }
+    return make_uint4(pack_h2(d[0], d[1]), pack_h2(d[2], d[3]), pack_h2(d[4], d[5]),
+                      pack_h2(d[6], d[7]));
+}
+
+template <bool INT4>
+__global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t *__restrict__ x,
+                                                    const void *__restrict__ wv,
+                                                    const float *__restrict__ sw,
+                                                    uint16_t *__restrict__ y, int M, int N, int K,
+                                                    int gs)
+{
+    const int8_t *__restrict__ w = static_cast<const int8_t *>(wv);
+    const uint8_t *__restrict__ w4 = static_cast<const uint8_t *>(wv);
+    const int G = INT4 ? K / gs : 1;
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][TB * 128];
     __shared__ __attribute__((aligned(16))) uint8_t ws[2][TB * 128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -58,8 +86,11 @@ __global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t *__restrict__
     const int nst = K / KS;
 
     // global loads of one stage: X 1024 chunks of 16 bytes (4 per thread),
-    // W 512 chunks of 16 int8 (2 per thread); rows past the end read zeros
+    // W 512 chunks of 16 int8 (2 per thread) or 256 chunks of 32 packed
+    // int4 codes (one per thread, with its group's scale); rows past the
+    // end read zeros
     uint4 xr[4], wr[2];
+    float wsc = 0.0f;
     auto load = [&](int s) __attribute__((always_inline)) {
         const int64_t k0 = (int64_t)s * KS;
 #pragma unroll
@@ -69,12 +100,21 @@ __global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t *__restrict__
             xr[p] = m < M ? *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + k0 + ch * 8)
                           : make_uint4(0u, 0u, 0u, 0u);
         }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int c = tid + 256 * p, r = c >> 2, ch = c & 3;
+        if constexpr (INT4) {
+            const int r = tid >> 1, half = tid & 1;  // 32 codes: k0 + 32 half .. + 31
             const int n = n0 + r;
-            wr[p] = n < N ? *reinterpret_cast<const uint4 *>(w + (int64_t)n * K + k0 + ch * 16)
+            const int64_t kc = k0 + 32 * half;
+            wr[0] = n < N ? *reinterpret_cast<const uint4 *>(w4 + (int64_t)n * (K / 2) + kc / 2)
                           : make_uint4(0u, 0u, 0u, 0u);
+            wsc = n < N ? sw[(int64_t)n * G + kc / gs] : 0.0f;
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int c = tid + 256 * p, r = c >> 2, ch = c & 3;
+                const int n = n0 + r;
+                wr[p] = n < N ? *reinterpret_cast<const uint4 *>(w + (int64_t)n * K + k0 + ch * 16)
+                              : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
     };
     auto store = [&](int buf) __attribute__((always_inline)) {
@@ -83,15 +123,24 @@ __global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t *__restrict__
             const int c = tid + 256 * p, r = c >> 3, ch = c & 7;
             *reinterpret_cast<uint4 *>(&xs[buf][r * 128 + swz16(r, ch) * 16]) = xr[p];
         }
+        if constexpr (INT4) {
+            const int r = tid >> 1, half = tid & 1;  // 32 codes -> fp16 chunks 4 half .. 4 half + 3
+            const uint32_t q[4] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w};
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int c = tid + 256 * p, r = c >> 2, ch = c & 3;   // 16 codes -> fp16 chunks 2ch, 2ch+1
-            const uint2 a = int8x4_to_half4(wr[p].x), b = int8x4_to_half4(wr[p].y);
-            const uint2 d = int8x4_to_half4(wr[p].z), e = int8x4_to_half4(wr[p].w);
-            *reinterpret_cast<uint4 *>(&ws[buf][r * 128 + swz16(r, 2 * ch) * 16]) =
-                make_uint4(a.x, a.y, b.x, b.y);
-            *reinterpret_cast<uint4 *>(&ws[buf][r * 128 + swz16(r, 2 * ch + 1) * 16]) =
-                make_uint4(d.x, d.y, e.x, e.y);
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint4 *>(&ws[buf][r * 128 + swz16(r, 4 * half + i) * 16]) =
+                    int4x8_dequant(q[i], wsc);
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int c = tid + 256 * p, r = c >> 2, ch = c & 3;   // 16 codes -> fp16 chunks 2ch, 2ch+1
+                const uint2 a = int8x4_to_half4(wr[p].x), b = int8x4_to_half4(wr[p].y);
+                const uint2 d = int8x4_to_half4(wr[p].z), e = int8x4_to_half4(wr[p].w);
+                *reinterpret_cast<uint4 *>(&ws[buf][r * 128 + swz16(r, 2 * ch) * 16]) =
+                    make_uint4(a.x, a.y, b.x, b.y);
+                *reinterpret_cast<uint4 *>(&ws[buf][r * 128 + swz16(r, 2 * ch + 1) * 16]) =
+                    make_uint4(d.x, d.y, e.x, e.y);
+            }
         }
     };
 
@@ -151,7 +200,18 @@ __global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t *__restrict__
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = nb + 8 * g + 4 * lh;
-                if (vec && n + 3 < N) {
+                if constexpr (INT4) {
+                    if (vec && n + 3 < N) {
+                        *reinterpret_cast<uint2 *>(y + (int64_t)m * N + n) =
+                            make_uint2(pack_h2(acc[j][i][4 * g], acc[j][i][4 * g + 1]),
+                                       pack_h2(acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]));
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < N)
+                                y[(int64_t)m * N + n + r] = f2h(acc[j][i][4 * g + r]);
+                    }
+                } else if (vec && n + 3 < N) {
                     const uint32_t p0 = pack_h2(acc[j][i][4 * g] * sw[n], acc[j][i][4 * g + 1] * sw[n + 1]);
                     const uint32_t p1 =
                         pack_h2(acc[j][i][4 * g + 2] * sw[n + 2], acc[j][i][4 * g + 3] * sw[n + 3]);
@@ -173,7 +233,16 @@ void launch_w8a16(const uint16_t *x, const int8_t *w, const float *sw, uint16_t 
                   int K, hipStream_t st)
 {
     const dim3 grid((unsigned)((N + TB - 1) / TB), (unsigned)((M + TB - 1) / TB));
-    hipLaunchKernelGGL(w8a16_kernel, grid, dim3(256), 0, st, x, w, sw, y, M, N, K);
+    hipLaunchKernelGGL(w8a16_kernel<false>, grid, dim3(256), 0, st, x, (const void *)w, sw, y, M,
+                       N, K, 0);
+}
+
+void launch_w4a16(const uint16_t *x, const uint8_t *w4, const float *sw, int gs, uint16_t *y, int M,
+                  int N, int K, hipStream_t st)
+{
+    const dim3 grid((unsigned)((N + TB - 1) / TB), (unsigned)((M + TB - 1) / TB));
+    hipLaunchKernelGGL(w8a16_kernel<true>, grid, dim3(256), 0, st, x, (const void *)w4, sw, y, M,
+                       N, K, gs);
 }
 
 }  // namespace w4a8

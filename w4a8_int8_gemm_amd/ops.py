@@ -242,3 +242,20 @@ def w8a16_gemm(x, wq, w_scale, out=None):
     with torch.cuda.device(x.device):
         check(lib().w8a16_gemm(_p(x), _p(wq), _p(w_scale), _p(out), M, N, K, _st(x)))
     return out
+
+
+def w4a16_gemm(x, w4, w_scale, group_size: int, out=None):
+    """Weight-only int4 comparison GEMM: y fp16 [M, N] = sum_k x[m,k] *
+    fp16(code[n,k] * w_scale[n, k // gs]); x fp16 [M, K], w4 uint8 [N, K/2],
+    w_scale fp32 [N, K/gs] (as from pack_weight_int4)."""
+    _need(x, torch.float16, "x", 2)
+    _need(w4, torch.uint8, "w4", 2)
+    _need(w_scale, torch.float32, "w_scale", 2)
+    M, K = x.shape
+    N = w4.shape[0]
+    if w4.shape[1] * 2 != K:
+        raise ValueError(f"weight shape {tuple(w4.shape)} does not match K={K}")
+    out = _out(out, (M, N), torch.float16, x, "out")
+    with torch.cuda.device(x.device):
+        check(lib().w4a16_gemm(_p(x), _p(w4), _p(w_scale), group_size, _p(out), M, N, K, _st(x)))
+    return out
