@@ -123,6 +123,24 @@ def test_extreme_int8_codes(torch_gpu, oracle):
     assert_equal(host(w.w8a8_gemm_i32(dev(xq), dev(wq))), c_ref, "int32 sums")
 
 
+def test_largest_k_extreme_codes(torch_gpu, oracle):
+    """K = 133120, the largest multiple of 64 the per-channel entry points
+    accept (127^2 K < 2^31): all-+-127 codes put the int32 sums within 0.02 %
+    of the int32 limit, through the int32 export and the fp16 epilogue."""
+    import w4a8_int8_gemm_amd as w
+    M, N, K = 32, 64, 133120
+    xq = np.full((M, K), 127, np.int8)
+    xq[1::2] = -127
+    wq = np.full((N, K), 127, np.int8)
+    wq[::3] = -127
+    c_ref = oracle.gemm_i32(xq, wq)
+    assert int(np.abs(c_ref).max()) == 127 * 127 * K
+    assert_equal(host(w.w8a8_gemm_i32(dev(xq), dev(wq))), c_ref, "int32 sums at the largest K")
+    sa, sw = synth.scales(M, 0, 3, 0, 1e-6), synth.scales(N, 0, 3, 1, 1e-3)
+    y = w.w8a8_gemm_pc(dev(xq), dev(sa), dev(wq), dev(sw))
+    assert_fp16_close(host(y), oracle.epilogue_pc(c_ref, sa, sw), what="fp16 y at the largest K")
+
+
 def test_zero_rows_and_empty(torch_gpu):
     import torch
     import w4a8_int8_gemm_amd as w
