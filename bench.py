@@ -316,15 +316,19 @@ def suite(reps):
     wq, sw = w.quantize_weight_int8(wt, 0)
     w4, s4 = w.pack_weight_int4(wt, 128)
     del wt
-    for M in (128, 1024, 4096, 8192):
+    for M in (1, 128, 1024, 4096, 8192):
         x = torch.from_numpy(synth.activations(M, K, seed=1)).cuda()
         y = torch.empty((M, N), dtype=torch.float16, device="cuda")
         xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
         xs = torch.empty((M, 1), dtype=torch.float32, device="cuda")
         f16 = lambda: w.check(L.w8a16_gemm(ptr(x), ptr(wq), ptr(sw), ptr(y), M, N, K, sp))
-        step = lambda: (w.check(L.quantize_act(ptr(x), M, K, 0, ptr(xq), ptr(xs), sp)),
-                        w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y), M, N,
-                                               K, sp)))
+        if M == 1:                       # the W8A8 decode path: int8_mv
+            step = lambda: w.check(L.int8_mv(ptr(x), ptr(wq), ptr(sw), ptr(y), N, K, None, None,
+                                             sp))
+        else:
+            step = lambda: (w.check(L.quantize_act(ptr(x), M, K, 0, ptr(xq), ptr(xs), sp)),
+                            w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y), M,
+                                                   N, K, sp)))
         f4 = lambda: w.check(L.w4a16_gemm(ptr(x), ptr(w4), ptr(s4), 128, ptr(y), M, N, K, sp))
         tf, t4, ts = b2b(f16), b2b(f4), b2b(step)
         ops = 2.0 * M * N * K

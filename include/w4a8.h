@@ -215,8 +215,10 @@ w4a8_status_t w4a8_gemm_partials(const int8_t *xq, const uint8_t *w4, int32_t gr
  * x fp16 [M, K], wq int8 [N, K] and w_scale fp32 [N] as produced by
  * quantize_weight_int8 with group_size 0, y fp16 [M, N].  Requires
  * K % 64 == 0 and M <= 65535 * 128; x, wq and y 16-byte aligned.  M == 0 or
- * N == 0 returns W4A8_OK with no launch.  Not part of the W8A8 hot path: it
- * exists to measure the W8A8 speed-up the pages report, on this GPU.
+ * N == 0 returns W4A8_OK with no launch.  M == 1 with K <= 16384 runs a
+ * matrix-vector kernel (the table's one-token row), larger M the GEMM.  Not
+ * part of the W8A8 hot path: it exists to measure the W8A8 speed-up the
+ * pages report, on this GPU.
  * ------------------------------------------------------------------------ */
 w4a8_status_t w8a16_gemm(const w4a8_f16 *x, const int8_t *wq, const float *w_scale,
                          w4a8_f16 *y, int64_t M, int64_t N, int64_t K, w4a8_stream_t stream);
@@ -228,7 +230,7 @@ w4a8_status_t w8a16_gemm(const w4a8_f16 *x, const int8_t *wq, const float *w_sca
  * fp32 accumulation.  x fp16 [M, K]; w4 uint8 [N, K/2] and w_scale fp32
  * [N, K/group_size] as produced by pack_weight_int4; group_size 64 or 128;
  * K % 64 == 0 and K % group_size == 0; M <= 65535 * 128.  Same conventions
- * as w8a16_gemm. */
+ * as w8a16_gemm, including the matrix-vector form at M == 1. */
 w4a8_status_t w4a16_gemm(const w4a8_f16 *x, const uint8_t *w4, const float *w_scale,
                          int32_t group_size, w4a8_f16 *y, int64_t M, int64_t N, int64_t K,
                          w4a8_stream_t stream);

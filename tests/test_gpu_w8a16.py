@@ -83,3 +83,20 @@ def test_w4a16_every_nibble(torch_gpu, oracle):
     y_ref, t_ref = oracle.w4a16(x, w4, s4, gs)
     y = w.w4a16_gemm(dev(x), dev(w4), dev(s4), gs)
     assert_fp16_close(host(y), y_ref, t_ref, K - 2, what="w4a16 y (every nibble)")
+
+
+@pytest.mark.parametrize("N,K", [(10240, 2560), (333, 4096), (7, 16384), (130, 64)])
+def test_weight_only_decode(torch_gpu, oracle, N, K):
+    """M == 1 takes the matrix-vector form (K <= 16384); same oracle, same bound."""
+    import w4a8_int8_gemm_amd as w
+    print(f"weight-only decode N={N} K={K}", flush=True)
+    x = synth.activations(1, K, seed=N)
+    wt = synth.weights(N, K, seed=K)
+    wq, sw = oracle.quantize_weight_int8(wt, 0)
+    y_ref, t_ref = oracle.w8a16(x, wq, sw)
+    y = w.w8a16_gemm(dev(x), dev(wq), dev(sw))
+    assert_fp16_close(host(y), y_ref, t_ref, K - 2, what="w8a16 decode")
+    w4, s4 = oracle.pack_weight_int4(wt, 64)
+    y_ref, t_ref = oracle.w4a16(x, w4, s4, 64)
+    y = w.w4a16_gemm(dev(x), dev(w4), dev(s4), 64)
+    assert_fp16_close(host(y), y_ref, t_ref, K - 2, what="w4a16 decode")

@@ -33,6 +33,7 @@ w4a8_status_t ok()
 constexpr int64_t kMaxDim = 0x7fffffff;
 constexpr int64_t kMaxKPerChannel = 133144;   // largest K with 127^2 * K < 2^31
 constexpr int64_t kMaxKMv = 32768;            // the token's codes are staged in LDS
+constexpr int64_t kMaxKWoMv = 16384;          // weight-only decode: the token as fp32 in LDS
 constexpr int64_t kMaxKGemm = int64_t(1) << 22; // a 256-row tile of K bytes stays below 2^30
 constexpr int64_t kMaxTiles = 0x7fffffff;     // 32 x 128 output tiles
 
@@ -484,8 +485,12 @@ w4a8_status_t w8a16_gemm(const w4a8_f16 *x, const int8_t *wq, const float *w_sca
     w4a8_status_t st = check_device();
     if (st != W4A8_OK)
         return st;
-    launch_w8a16(reinterpret_cast<const uint16_t *>(x), wq, w_scale,
-                 reinterpret_cast<uint16_t *>(y), (int)M, (int)N, (int)K, (hipStream_t)stream);
+    if (M == 1 && K <= kMaxKWoMv)                     // one token: the matrix-vector form
+        launch_wo_mv(false, reinterpret_cast<const uint16_t *>(x), wq, w_scale, 0,
+                     reinterpret_cast<uint16_t *>(y), (int)N, (int)K, (hipStream_t)stream);
+    else
+        launch_w8a16(reinterpret_cast<const uint16_t *>(x), wq, w_scale,
+                     reinterpret_cast<uint16_t *>(y), (int)M, (int)N, (int)K, (hipStream_t)stream);
     return check_launch(fn);
 }
 
@@ -513,7 +518,11 @@ w4a8_status_t w4a16_gemm(const w4a8_f16 *x, const uint8_t *w4, const float *w_sc
     w4a8_status_t st = check_device();
     if (st != W4A8_OK)
         return st;
-    launch_w4a16(reinterpret_cast<const uint16_t *>(x), w4, w_scale, (int)group_size,
-                 reinterpret_cast<uint16_t *>(y), (int)M, (int)N, (int)K, (hipStream_t)stream);
+    if (M == 1 && K <= kMaxKWoMv)                     // one token: the matrix-vector form
+        launch_wo_mv(true, reinterpret_cast<const uint16_t *>(x), w4, w_scale, (int)group_size,
+                     reinterpret_cast<uint16_t *>(y), (int)N, (int)K, (hipStream_t)stream);
+    else
+        launch_w4a16(reinterpret_cast<const uint16_t *>(x), w4, w_scale, (int)group_size,
+                     reinterpret_cast<uint16_t *>(y), (int)M, (int)N, (int)K, (hipStream_t)stream);
     return check_launch(fn);
 }

@@ -54,5 +54,8 @@ void launch_w8a16(const uint16_t *x, const int8_t *w, const float *sw, uint16_t 
 // w_scale[n,g]))) with packed int4 weights [N, K/2] (K % 64 == 0, K % gs == 0).
 void launch_w4a16(const uint16_t *x, const uint8_t *w4, const float *sw, int gs, uint16_t *y, int M,
                   int N, int K, hipStream_t st);
+// Their decode (M = 1) form: y[n] for one fp16 token x [K] (K <= 16384).
+void launch_wo_mv(bool int4, const uint16_t *x, const void *w, const float *sw, int gs, uint16_t *y,
+                  int N, int K, hipStream_t st);
 
 }  // namespace w4a8

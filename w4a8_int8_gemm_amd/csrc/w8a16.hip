@@ -227,7 +227,91 @@ __global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t *__restrict__
     }
 }
 
+// Decode (M = 1) form of the weight-only products: the token is staged in
+// LDS as fp32, 16 lanes share a weight row (16-byte chunks, 16 int8 or 32
+// int4 codes each, up to 8 chunks per lane in flight), products accumulate
+// in fp32 and the row's lanes add their sums.  Weights are dequantized as in
+// the GEMM (int8: exact, scale at the end; int4: fp16(fl32(code * s))).
+template <bool INT4>
+__global__ __launch_bounds__(256) void wo_mv_kernel(const uint16_t *__restrict__ x,
+                                                    const void *__restrict__ wv,
+                                                    const float *__restrict__ sw,
+                                                    uint16_t *__restrict__ y, int N, int K, int gs)
+{
+    extern __shared__ __attribute__((aligned(16))) float xf[];   // K floats
+    const int tid = threadIdx.x;
+    for (int c = tid; c < K / 8; c += 256) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(x + c * 8);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xf[c * 8 + 2 * i] = h2f((uint16_t)(u[i] & 0xffffu));
+            xf[c * 8 + 2 * i + 1] = h2f((uint16_t)(u[i] >> 16));
+        }
+    }
+    __syncthreads();
+    const int n = blockIdx.x * 16 + (tid >> 4), lr = tid & 15;
+    const int nr = min(n, N - 1);
+    constexpr int KPC = INT4 ? 32 : 16;               // codes per 16-byte chunk
+    const int nch = K / KPC;
+    const uint8_t *wr = static_cast<const uint8_t *>(wv) + (int64_t)nr * (K / (INT4 ? 2 : 1));
+    const int G = INT4 ? K / gs : 1;
+    float acc = 0.0f;
+    for (int base = 0; base < nch; base += 16 * 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = base + lr + 16 * j;
+            v[j] = c < nch ? *reinterpret_cast<const uint4 *>(wr + c * 16) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = base + lr + 16 * j;
+            if (c >= nch)
+                continue;
+            const uint32_t q[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            const float *xc = xf + c * KPC;
+            if constexpr (INT4) {
+                const float s = sw[(int64_t)nr * G + (c * KPC) / gs];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 h = int4x8_dequant(q[i], s);
+                    const uint32_t hh[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc = fmaf(xc[8 * i + 2 * e], h2f((uint16_t)(hh[e] & 0xffffu)), acc);
+                        acc = fmaf(xc[8 * i + 2 * e + 1], h2f((uint16_t)(hh[e] >> 16)), acc);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc = fmaf(xc[4 * i + e], (float)(int8_t)(q[i] >> (8 * e)), acc);
+            }
+        }
+    }
+    // sum over the row's 16 lanes
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1)
+        acc += __shfl_xor(acc, o, 16);
+    if (lr == 0 && n < N)
+        y[n] = f2h(INT4 ? acc : acc * sw[n]);
+}
+
 }  // namespace
+
+void launch_wo_mv(bool int4, const uint16_t *x, const void *w, const float *sw, int gs, uint16_t *y,
+                  int N, int K, hipStream_t st)
+{
+    const unsigned blocks = (unsigned)((N + 15) / 16);
+    const size_t lds = (size_t)K * sizeof(float);
+    if (int4)
+        hipLaunchKernelGGL(wo_mv_kernel<true>, dim3(blocks), dim3(256), lds, st, x, w, sw, y, N, K, gs);
+    else
+        hipLaunchKernelGGL(wo_mv_kernel<false>, dim3(blocks), dim3(256), lds, st, x, w, sw, y, N, K, 0);
+}
 
 void launch_w8a16(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, int M, int N,
                   int K, hipStream_t st)
