@@ -31,6 +31,11 @@ PC_SHAPES = [
     (1500, 8196, 320), (1500, 8200, 1280),
     # 256x160 tiles, one round over the CUs, ragged M
     (1000, 10240, 256),
+    # few tokens: 32x32 and 64x64 tiles, N ragged against them (scalar stores
+    # where N % 8 != 0), a K tail; the M = 32 / 64 rows of the N=10240 K=2560
+    # layer
+    (32, 1000, 448), (31, 1030, 320), (48, 1030, 448), (33, 2051, 192),
+    (32, 10240, 2560), (64, 10240, 2560),
 ]
 
 
@@ -56,7 +61,9 @@ def test_gemm_i32_and_pc(torch_gpu, oracle, M, N, K):
 # (gs = 64 only).
 PG_SHAPES = [(16, 512, 256), (3, 100, 384), (200, 300, 640), (257, 321, 512),
              (70, 200, 320), (1024, 4096, 256), (2048, 8192, 256), (1800, 6100, 384),
-             (1800, 6100, 448)]
+             (1800, 6100, 448),
+             # few tokens: 32x32 tiles, N ragged against them
+             (31, 1000, 384), (32, 1030, 256)]
 
 
 @pytest.mark.parametrize("gs", [64, 128])

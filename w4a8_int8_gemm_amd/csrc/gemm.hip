@@ -936,12 +936,23 @@ void launch_mode(const GemmArgs &a, hipStream_t st)
     const int64_t t256x160 = (int64_t)((a.M + 255) / 256) * ((a.N + 159) / 160);
     const int64_t t256x128 = (int64_t)((a.M + 255) / 256) * ((a.N + 127) / 128);
     const int64_t t128x128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+    // Few tokens: the weights are streamed once and the output is small, so
+    // the tile count decides how many compute units pull weights.  32x32
+    // single-wave tiles (int8 weights) and 64x64 ones (per-channel) give four
+    // and two times the tiles of 32x128 / 64x128; the narrow tiles did not pay
+    // for W4A8, nor for the per-group modes above 32 tokens.
     if (a.M <= 32) {
-        launch_cfg<32, 128, 1, 4, MODE, GS>(a, st);
+        if constexpr (ModeTraits<MODE>::int4)
+            launch_cfg<32, 128, 1, 4, MODE, GS>(a, st);
+        else
+            launch_cfg<32, 32, 1, 1, MODE, GS>(a, st);
         return;
     }
     if (a.M <= 64) {
-        launch_cfg<64, 128, 2, 2, MODE, GS>(a, st);
+        if constexpr (pergroup)
+            launch_cfg<64, 128, 2, 2, MODE, GS>(a, st);
+        else
+            launch_cfg<64, 64, 1, 2, MODE, GS>(a, st);
         return;
     }
     if constexpr (!pergroup) {
