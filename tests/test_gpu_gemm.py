@@ -36,6 +36,10 @@ PC_SHAPES = [
     # layer
     (32, 1000, 448), (31, 1030, 320), (48, 1030, 448), (33, 2051, 192),
     (32, 10240, 2560), (64, 10240, 2560),
+    # few tokens with N large enough that each workgroup streams several
+    # tiles (the four-stage ring across tile boundaries), with stages per
+    # tile below and above the ring depth
+    (8, 49160, 256), (8, 49152, 640), (40, 40968, 192),
 ]
 
 

@@ -21,7 +21,8 @@
 //    of rows m), which matches their per-column scales and int32 stores.
 //    This MFMA sustains close to the int8 peak with a single wave per SIMD,
 //    which the large per-wave tiles need (they keep LDS reads per MFMA low).
-//  * K advances in stages of 128 bytes through a ring of three LDS buffers.
+//  * K advances in stages of 128 bytes through a ring of R = 3 LDS buffers
+//    (R = 4 for the few-token per-channel tiles).
 //    Stages are copied from global memory straight into LDS (buffer loads
 //    with the lds modifier, 16-byte chunks XOR-swizzled per row); the copies
 //    of one stage are spread over four k-steps between the MFMAs, and the
@@ -230,7 +231,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     // conservative)
     constexpr int ND = XB + WB + SA_I / NW + SW_I / NW;
     // The copies of stage u are spread over four k-steps: part A in step 3 of
-    // iteration u-3, parts 0..2 in steps 0..2 of iteration u-2.  Scale copies
+    // iteration u-R, parts 0..2 in steps 0..2 of iteration u-R+1 (R, the LDS
+    // ring depth, is 3 except for the few-token tiles below).  Scale copies
     // never go in part A (the group fold after step 3 still reads the scales
     // in that buffer).  int4 weights are register-staged; their compiler
     // tracked loads make it wait for every earlier copy before the unpack, so
@@ -252,8 +254,13 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
     constexpr int ESN = (MODE == GemmMode::PC) ? BM + BN : (MODE == GemmMode::W4 ? BM : 0);
     constexpr int EW = (ESN + 64 * NW - 1) / (64 * NW);   // copy instructions per wave
 
-    __shared__ __attribute__((aligned(1024))) int8_t xs[3 * XBUF];
-    __shared__ __attribute__((aligned(1024))) int8_t ws[3 * WBUF];
+    // LDS ring depth: three stages, four for the few-token per-channel tiles
+    // (their stages are small, and one more stage in flight shortens the
+    // waits on weights that come from HBM)
+    constexpr int RING = (!T::pergroup && !T::int4 && BN <= 64) ? 4 : 3;
+    static_assert((RING - 2) * ND + CA < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) int8_t xs[RING * XBUF];
+    __shared__ __attribute__((aligned(1024))) int8_t ws[RING * WBUF];
     // Group scales have a ring of their own, one slot per stage: a group is
     // folded after its last k-step, which for the last group of a stage comes
     // after the barrier of its iteration, while a wave that is already past
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         int v;         // stage in this workgroup's stream (clamped to U - 1)
         int s;         // stage within its tile
         int tile;      // tile within this workgroup's list
-        int buf;       // LDS buffer (the unclamped stage index mod 3)
+        int buf;       // LDS buffer (the unclamped stage index mod RING)
         int sb;        // scale ring slot (the unclamped stage index mod SR)
         int m0, n0;    // tile origin
         v4i rx, rw;    // buffer resources of the tile's X rows and int8 W rows
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
             c.rw = make_rsrc(wb + (int64_t)c.n0 * K, (uint32_t)(min(BN, N - c.n0) * K));
     };
     auto advance = [&](Src &c) __attribute__((always_inline)) {
-        c.buf = c.buf == 2 ? 0 : c.buf + 1;
+        c.buf = c.buf == RING - 1 ? 0 : c.buf + 1;
         c.sb = c.sb == SR - 1 ? 0 : c.sb + 1;
         if (c.v + 1 < U) {                            // past the end: repeat the last stage
             ++c.v;
@@ -765,19 +772,20 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
         }
     };
 
-    // ---- pipeline.  Stage u of the stream lives in LDS buffer u % 3.  Its
-    // copies are issued in four parts: part A during step 3 of iteration u-3,
-    // right after the barrier that frees the buffer, and parts 0-2 during
-    // steps 0-2 of iteration u-2 (int4 weights: loaded into registers in
-    // iteration u-2 and unpacked to LDS before the barrier of iteration u-1).
-    // Iteration u: steps 0-2 from buffer u%3; wait for stage u+1 and barrier;
-    // step 3, which also reads the first fragments of stage u+1; after the
-    // last stage of a tile, its epilogue.  Every iteration issues the same
-    // copies -- past the end of the stream they repeat the last stage into a
-    // buffer nobody reads -- so every wait count is a constant.
+    // ---- pipeline.  Stage u of the stream lives in LDS buffer u % R (R =
+    // RING).  Its copies are issued in four parts: part A during step 3 of
+    // iteration u-R, right after the barrier that frees the buffer, and parts
+    // 0-2 during steps 0-2 of iteration u-R+1 (int4 weights, R = 3: loaded
+    // into registers in iteration u-2 and unpacked to LDS before the barrier
+    // of iteration u-1).  Iteration u: steps 0-2 from buffer u%R; wait for
+    // stage u+1 (the R-2 later stages' copies may stay in flight) and
+    // barrier; step 3, which also reads the first fragments of stage u+1;
+    // after the last stage of a tile, its epilogue.  Every iteration issues
+    // the same copies -- past the end of the stream they repeat the last
+    // stage into a buffer nobody reads -- so every wait count is a constant.
     auto main_loop = [&](auto KFULL) __attribute__((always_inline)) {
         constexpr bool kfull = decltype(KFULL)::value;   // K % 128 == 0: every k-step exists
-        Src cp;                                       // stage 0, then 1, 2 (prologue)
+        Src cp;                                       // stages 0 .. R-1 (prologue)
         cp.v = 0; cp.s = 0; cp.buf = 0; cp.sb = 0;
         set_tile(cp, 0);
         int cm0 = cp.m0, cn0 = cp.n0, ctile = 0;      // the tile being computed
@@ -793,18 +801,23 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
             w4_load(cp);
         issue_copies(cp, cp.buf, 0, NCW, KFULL);
         advance(cp);
+#pragma unroll
+        for (int e = 3; e < RING; ++e) {              // stages 2 .. RING - 2
+            issue_copies(cp, cp.buf, 0, NCW, KFULL);
+            advance(cp);
+        }
         issue_copies(cp, cp.buf, 0, CA, KFULL);
-        Src c2 = cp;                                  // stage u+2: parts 0-2 in iteration u
+        Src c2 = cp;                                  // stage u+R-1: parts 0-2 in iteration u
         advance(cp);
-        Src c3 = cp;                                  // stage u+3: part A in iteration u
-        wait_vmcnt<ND + CA>();
+        Src c3 = cp;                                  // stage u+R: part A in iteration u
+        wait_vmcnt<(RING - 2) * ND + CA>();
         lds_barrier();
         read_frag(f0, 0, 0);
 
         int b = 0, s = 0;                             // buffer and in-tile stage of iteration u
         int sb = 0;                                   // scale ring slot of iteration u
         for (int u = 0; u < U; ++u) {
-            const int b1 = b == 2 ? 0 : b + 1;
+            const int b1 = b == RING - 1 ? 0 : b + 1;
             const int ks0 = s * 4;
             auto step = [&](auto TC, const Src &src, int c0, int n) __attribute__((always_inline)) {
                 constexpr int t = decltype(TC)::value;
@@ -858,7 +871,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
             // stage u+1 complete and visible; buffer b free
             if constexpr (T::int4)
                 w4_store(b1);
-            wait_vmcnt<ND>();
+            wait_vmcnt<(RING - 2) * ND>();
             lds_barrier();
             if constexpr (T::int4)
                 w4_load(c2);
@@ -866,7 +879,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs args, int ti
 
             if (s + 1 == nstage) {                    // the tile is done
                 if constexpr (EW > 0) {
-                    if (nstage < 3) {                 // its scales may still be in flight
+                    if (nstage < RING) {              // its scales may still be in flight
                         wait_vmcnt<0>();
                         lds_barrier();
                     }
