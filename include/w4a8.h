@@ -113,6 +113,9 @@ w4a8_status_t pack_weight_int4(const w4a8_f16 *w, int64_t N, int64_t K, int32_t 
  * with the sum exact in int32 and the rescale in fp32, rounded to nearest
  * even.  xq int8 [M, K], x_scale fp32 [M], wq int8 [N, K], w_scale fp32 [N],
  * y fp16 [M, N].  Requires K % 64 == 0 and K <= 133144 (so 127^2 K < 2^31).
+ * For 1 <= M <= 4 with M*K <= 65536 the product runs as a matrix-vector form
+ * that streams whole weight rows (the tokens' codes staged on chip); the
+ * arithmetic, and so every output bit, is the same as the GEMM's.
  * ------------------------------------------------------------------------ */
 w4a8_status_t w8a8_gemm_pc(const int8_t *xq, const float *x_scale, const int8_t *wq,
                            const float *w_scale, w4a8_f16 *y, int64_t M, int64_t N, int64_t K,

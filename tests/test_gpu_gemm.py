@@ -40,6 +40,11 @@ PC_SHAPES = [
     # tiles (the four-stage ring across tile boundaries), with stages per
     # tile below and above the ring depth
     (8, 49160, 256), (8, 49152, 640), (40, 40968, 192),
+    # 1-4 tokens: the matrix-vector form, one shape per lane split (K / 16
+    # chunks <= 64, 128, 160, 256, more), N ragged against its 16 or 4 rows
+    # per workgroup; M * K at 65536 (last one on this path) and just above
+    (2, 1001, 1024), (4, 333, 2048), (3, 10240, 2560), (1, 4099, 4096), (4, 777, 16384),
+    (2, 5, 32768), (4, 129, 16448),
 ]
 
 

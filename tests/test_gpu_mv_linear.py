@@ -42,7 +42,7 @@ def test_int8_mv_zero_token(torch_gpu, oracle):
     assert np.all(host(y) == 0) and np.all(host(xq) == 0) and host(xs)[0] == 0
 
 
-@pytest.mark.parametrize("M", [1, 2, 5, 64, 300])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 64, 300])
 def test_linear_pc_end_to_end(torch_gpu, oracle, M):
     """GPU: quantize_weight_int8 + linear.  Oracle: its own quantizer + GEMM."""
     import w4a8_int8_gemm_amd as w

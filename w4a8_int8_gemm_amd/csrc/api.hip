@@ -36,6 +36,10 @@ constexpr int64_t kMaxKMv = 32768;            // the token's codes are staged in
 constexpr int64_t kMaxKWoMv = 16384;          // weight-only decode: the token as fp32 in LDS
 constexpr int64_t kMaxKGemm = int64_t(1) << 22; // a 256-row tile of K bytes stays below 2^30
 constexpr int64_t kMaxTiles = 0x7fffffff;     // 32 x 128 output tiles
+// Few-token per-channel product (the weight rows streamed whole): up to 4
+// tokens, whose codes are staged in LDS
+constexpr int64_t kMaxMFew = 4;
+constexpr int64_t kMaxFewCodes = 65536;       // M * K bytes
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -206,6 +210,24 @@ w4a8_status_t run_gemm(const char *fn, GemmMode mode, const GemmArgs &a, w4a8_st
     return check_launch(fn);
 }
 
+// The per-channel product on checked arguments: up to four tokens as the
+// few-token matrix-vector form (same arithmetic), else the GEMM.
+w4a8_status_t run_pc(const char *fn, const int8_t *xq, const float *xs, const int8_t *wq,
+                     const float *sw, w4a8_f16 *y, int64_t M, int64_t N, int64_t K,
+                     w4a8_stream_t stream)
+{
+    if (M >= 1 && M <= kMaxMFew && M * K <= kMaxFewCodes) {
+        if (N == 0)
+            return ok();
+        w4a8_status_t st = check_device();
+        if (st != W4A8_OK)
+            return st;
+        launch_few_pc(xq, xs, wq, sw, y, (int)M, (int)N, (int)K, (hipStream_t)stream);
+        return check_launch(fn);
+    }
+    return run_gemm(fn, GemmMode::PC, make_args(xq, xs, wq, sw, y, M, N, K, 0), stream);
+}
+
 w4a8_status_t run_quant(const char *fn, const uint16_t *x, int64_t rows, int64_t K, int gs,
                         float qmax, void *q, float *scale, bool int4, w4a8_stream_t stream)
 {
@@ -276,8 +298,7 @@ w4a8_status_t w8a8_gemm_pc(const int8_t *xq, const float *x_scale, const int8_t 
                                   true);
     if (st != W4A8_OK)
         return st;
-    return run_gemm("w8a8_gemm_pc", GemmMode::PC, make_args(xq, x_scale, wq, w_scale, y, M, N, K, 0),
-                    stream);
+    return run_pc("w8a8_gemm_pc", xq, x_scale, wq, w_scale, y, M, N, K, stream);
 }
 
 w4a8_status_t w8a8_gemm_pg(const int8_t *xq, const float *x_scale, const int8_t *wq,
@@ -416,8 +437,7 @@ w4a8_status_t linear(w4a8_mode_t mode, const w4a8_f16 *x, int64_t M, int64_t K, 
         return st;
     switch (mode) {
     case W4A8_MODE_W8A8_PC:
-        return run_gemm("linear", GemmMode::PC,
-                        make_args(xq, xs, w, w_scale, y, M, N, K, 0), stream);
+        return run_pc("linear", xq, xs, static_cast<const int8_t *>(w), w_scale, y, M, N, K, stream);
     case W4A8_MODE_W8A8_PG:
         return run_gemm("linear", GemmMode::PG,
                         make_args(xq, xs, w, w_scale, y, M, N, K, group_size), stream);

@@ -37,6 +37,12 @@ struct GemmArgs {
 
 void launch_gemm(GemmMode mode, const GemmArgs &a, hipStream_t st);
 
+// Few-token per-channel product (1 <= M <= 4, M * K <= 64 KiB): the weight
+// rows streamed whole against the tokens' codes in LDS; equals the
+// per-channel GEMM bit for bit.
+void launch_few_pc(const int8_t *xq, const float *xs, const int8_t *w, const float *sw,
+                   uint16_t *y, int M, int N, int K, hipStream_t st);
+
 // Decode matrix-vector: quantize the token, y[n] = rescale(sum_k q[k] w[n,k]).
 void launch_int8_mv(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, int N,
                     int K, int8_t *xq_out, float *xs_out, hipStream_t st);

@@ -380,6 +380,123 @@ void launch_int8_mv(const uint16_t *x, const int8_t *w, const float *sw, uint16_
         launch_x<64, 16>(x, w, sw, y, N, K, xq_out, xs_out, st);
 }
 
+namespace {
+
+// Few tokens, per-channel scales: the GEMM's arithmetic in the decode
+// kernel's shape.  The weight rows are streamed whole (LPR lanes per row, CPL
+// 16-byte chunks per lane in flight) and each chunk is dotted with the codes
+// of all M <= MT tokens, staged in LDS; per token one exact int32 sum per row,
+// then the GEMM epilogue's rescale, so the result equals the GEMM's bit for bit.
+template <int MT, int LPR, int CPL>
+__global__ __launch_bounds__(256) void few_pc_kernel(const int8_t *__restrict__ xq,
+                                                     const float *__restrict__ xs,
+                                                     const int8_t *__restrict__ w,
+                                                     const float *__restrict__ sw,
+                                                     uint16_t *__restrict__ y, int M, int N, int K)
+{
+    extern __shared__ __attribute__((aligned(16))) int8_t xq_s[];   // M * K bytes
+    constexpr int RPB = 256 / LPR;                  // rows per workgroup
+    const int tid = threadIdx.x;
+    const int n = blockIdx.x * RPB + tid / LPR;
+    const int lr = tid % LPR;
+    const int nch = K >> 4;                         // 16-byte chunks per row
+    const bool row_ok = n < N;
+    const uint4 *wr = reinterpret_cast<const uint4 *>(w + (int64_t)min(n, N - 1) * K);
+
+    uint4 wv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lr + LPR * j;
+        wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // the tokens' codes, M rows of K bytes, into LDS
+    const int xch = (M * K) >> 4;
+    for (int c = tid; c < xch; c += 256)
+        reinterpret_cast<uint4 *>(xq_s)[c] = reinterpret_cast<const uint4 *>(xq)[c];
+    __syncthreads();
+
+    int acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        acc[t] = 0;
+    for (int base = 0;; base += LPR * CPL) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = base + lr + LPR * j;
+            if (c < nch) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    if (t < M) {
+                        const uint4 q = *reinterpret_cast<const uint4 *>(xq_s + t * K + c * 16);
+                        int a = acc[t];
+                        a = __builtin_amdgcn_sdot4((int)wv[j].x, (int)q.x, a, false);
+                        a = __builtin_amdgcn_sdot4((int)wv[j].y, (int)q.y, a, false);
+                        a = __builtin_amdgcn_sdot4((int)wv[j].z, (int)q.z, a, false);
+                        acc[t] = __builtin_amdgcn_sdot4((int)wv[j].w, (int)q.w, a, false);
+                    }
+                }
+            }
+        }
+        const int next = base + LPR * CPL;
+        if (next >= nch)
+            break;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = next + lr + LPR * j;
+            wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    const float swn = sw[min(n, N - 1)];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t < M) {
+            const int a = group_sum_i32<LPR>(acc[t]);
+            if (lr == 0 && row_ok)
+                y[(int64_t)t * N + n] = f2h(rescale_pc(a, xs[t], swn));
+        }
+    }
+}
+
+template <int MT, int LPR, int CPL>
+void launch_few(const int8_t *xq, const float *xs, const int8_t *w, const float *sw, uint16_t *y,
+                int M, int N, int K, hipStream_t st)
+{
+    constexpr int RPB = 256 / LPR;
+    const unsigned blocks = (unsigned)((N + RPB - 1) / RPB);
+    hipLaunchKernelGGL((few_pc_kernel<MT, LPR, CPL>), dim3(blocks), dim3(256), (size_t)M * K, st,
+                       xq, xs, w, sw, y, M, N, K);
+}
+
+template <int MT>
+void launch_few_m(const int8_t *xq, const float *xs, const int8_t *w, const float *sw, uint16_t *y,
+                  int M, int N, int K, hipStream_t st)
+{
+    const int nch = K / 16;
+    if (nch <= 16 * 4)
+        launch_few<MT, 16, 4>(xq, xs, w, sw, y, M, N, K, st);
+    else if (nch <= 16 * 8)
+        launch_few<MT, 16, 8>(xq, xs, w, sw, y, M, N, K, st);
+    else if (nch <= 16 * 10)
+        launch_few<MT, 16, 10>(xq, xs, w, sw, y, M, N, K, st);
+    else if (nch <= 16 * 16)
+        launch_few<MT, 16, 16>(xq, xs, w, sw, y, M, N, K, st);
+    else
+        launch_few<MT, 64, 16>(xq, xs, w, sw, y, M, N, K, st);
+}
+
+}  // namespace
+
+void launch_few_pc(const int8_t *xq, const float *xs, const int8_t *w, const float *sw,
+                   uint16_t *y, int M, int N, int K, hipStream_t st)
+{
+    if (M <= 1)
+        launch_few_m<1>(xq, xs, w, sw, y, M, N, K, st);
+    else if (M <= 2)
+        launch_few_m<2>(xq, xs, w, sw, y, M, N, K, st);
+    else
+        launch_few_m<4>(xq, xs, w, sw, y, M, N, K, st);
+}
+
 void launch_mv_group(bool int4, int gs, const uint16_t *x, const uint8_t *w, const float *sw,
                      uint16_t *y, int N, int K, hipStream_t st)
 {
