@@ -44,7 +44,7 @@ PC_SHAPES = [
     # chunks <= 64, 128, 160, 256, more), N ragged against its 16 or 4 rows
     # per workgroup; M * K at 65536 (last one on this path) and just above
     (2, 1001, 1024), (4, 333, 2048), (3, 10240, 2560), (1, 4099, 4096), (4, 777, 16384),
-    (2, 5, 32768), (4, 129, 16448),
+    (2, 5, 32768), (4, 129, 16448), (3, 4099, 14336), (4, 4096, 12288),
 ]
 
 

@@ -384,10 +384,11 @@ namespace {
 
 // Few tokens, per-channel scales: the GEMM's arithmetic in the decode
 // kernel's shape.  The weight rows are streamed whole (LPR lanes per row, CPL
-// 16-byte chunks per lane in flight) and each chunk is dotted with the codes
-// of all M <= MT tokens, staged in LDS; per token one exact int32 sum per row,
-// then the GEMM epilogue's rescale, so the result equals the GEMM's bit for bit.
-template <int MT, int LPR, int CPL>
+// 16-byte chunks per lane in flight, RPT rows per lane group) and each chunk
+// is dotted with the codes of all M <= MT tokens, staged in LDS; per token one
+// exact int32 sum per row, then the GEMM epilogue's rescale, so the result
+// equals the GEMM's bit for bit.
+template <int MT, int LPR, int CPL, int RPT>
 __global__ __launch_bounds__(256) void few_pc_kernel(const int8_t *__restrict__ xq,
                                                      const float *__restrict__ xs,
                                                      const int8_t *__restrict__ w,
@@ -395,30 +396,36 @@ __global__ __launch_bounds__(256) void few_pc_kernel(const int8_t *__restrict__ 
                                                      uint16_t *__restrict__ y, int M, int N, int K)
 {
     extern __shared__ __attribute__((aligned(16))) int8_t xq_s[];   // M * K bytes
-    constexpr int RPB = 256 / LPR;                  // rows per workgroup
+    constexpr int RPB = 256 / LPR;                  // rows per pass of the workgroup
     const int tid = threadIdx.x;
-    const int n = blockIdx.x * RPB + tid / LPR;
     const int lr = tid % LPR;
-    const int nch = K >> 4;                         // 16-byte chunks per row
-    const bool row_ok = n < N;
-    const uint4 *wr = reinterpret_cast<const uint4 *>(w + (int64_t)min(n, N - 1) * K);
-
-    uint4 wv[CPL];
+    const int nch = K >> 4;
+    int n[RPT];
+    const uint4 *wr[RPT];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int c = lr + LPR * j;
-        wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+    for (int r = 0; r < RPT; ++r) {
+        n[r] = blockIdx.x * (RPB * RPT) + r * RPB + tid / LPR;
+        wr[r] = reinterpret_cast<const uint4 *>(w + (int64_t)min(n[r], N - 1) * K);
     }
-    // the tokens' codes, M rows of K bytes, into LDS
+    uint4 wv[RPT][CPL];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = lr + LPR * j;
+            wv[r][j] = (c < nch) ? load_nt(wr[r] + c) : make_uint4(0u, 0u, 0u, 0u);
+        }
     const int xch = (M * K) >> 4;
     for (int c = tid; c < xch; c += 256)
         reinterpret_cast<uint4 *>(xq_s)[c] = reinterpret_cast<const uint4 *>(xq)[c];
     __syncthreads();
 
-    int acc[MT];
+    int acc[RPT][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-        acc[t] = 0;
+    for (int r = 0; r < RPT; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            acc[r][t] = 0;
     for (int base = 0;; base += LPR * CPL) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
@@ -428,11 +435,14 @@ __global__ __launch_bounds__(256) void few_pc_kernel(const int8_t *__restrict__ 
                 for (int t = 0; t < MT; ++t) {
                     if (t < M) {
                         const uint4 q = *reinterpret_cast<const uint4 *>(xq_s + t * K + c * 16);
-                        int a = acc[t];
-                        a = __builtin_amdgcn_sdot4((int)wv[j].x, (int)q.x, a, false);
-                        a = __builtin_amdgcn_sdot4((int)wv[j].y, (int)q.y, a, false);
-                        a = __builtin_amdgcn_sdot4((int)wv[j].z, (int)q.z, a, false);
-                        acc[t] = __builtin_amdgcn_sdot4((int)wv[j].w, (int)q.w, a, false);
+#pragma unroll
+                        for (int r = 0; r < RPT; ++r) {
+                            int a = acc[r][t];
+                            a = __builtin_amdgcn_sdot4((int)wv[r][j].x, (int)q.x, a, false);
+                            a = __builtin_amdgcn_sdot4((int)wv[r][j].y, (int)q.y, a, false);
+                            a = __builtin_amdgcn_sdot4((int)wv[r][j].z, (int)q.z, a, false);
+                            acc[r][t] = __builtin_amdgcn_sdot4((int)wv[r][j].w, (int)q.w, a, false);
+                        }
                     }
                 }
             }
@@ -441,18 +451,23 @@ __global__ __launch_bounds__(256) void few_pc_kernel(const int8_t *__restrict__ 
         if (next >= nch)
             break;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int c = next + lr + LPR * j;
-            wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-    const float swn = sw[min(n, N - 1)];
+        for (int r = 0; r < RPT; ++r)
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        if (t < M) {
-            const int a = group_sum_i32<LPR>(acc[t]);
-            if (lr == 0 && row_ok)
-                y[(int64_t)t * N + n] = f2h(rescale_pc(a, xs[t], swn));
+            for (int j = 0; j < CPL; ++j) {
+                const int c = next + lr + LPR * j;
+                wv[r][j] = (c < nch) ? load_nt(wr[r] + c) : make_uint4(0u, 0u, 0u, 0u);
+            }
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const float swn = sw[min(n[r], N - 1)];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (t < M) {
+                const int a = group_sum_i32<LPR>(acc[r][t]);
+                if (lr == 0 && n[r] < N)
+                    y[(int64_t)t * N + n[r]] = f2h(rescale_pc(a, xs[t], swn));
+            }
         }
     }
 }
@@ -461,9 +476,12 @@ template <int MT, int LPR, int CPL>
 void launch_few(const int8_t *xq, const float *xs, const int8_t *w, const float *sw, uint16_t *y,
                 int M, int N, int K, hipStream_t st)
 {
-    constexpr int RPB = 256 / LPR;
+    // two rows per lane group (each token chunk read from LDS serves both)
+    // where it measured faster: four tokens at 64 lanes per row (K > 4096)
+    constexpr int RPT = (MT == 4 && LPR == 64) ? 2 : 1;
+    constexpr int RPB = 256 / LPR * RPT;
     const unsigned blocks = (unsigned)((N + RPB - 1) / RPB);
-    hipLaunchKernelGGL((few_pc_kernel<MT, LPR, CPL>), dim3(blocks), dim3(256), (size_t)M * K, st,
+    hipLaunchKernelGGL((few_pc_kernel<MT, LPR, CPL, RPT>), dim3(blocks), dim3(256), (size_t)M * K, st,
                        xq, xs, w, sw, y, M, N, K);
 }
 
