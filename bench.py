@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="untimed steps for this long before the warm-up steps, so the GPU "
+                         "has left its idle clocks (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
@@ -453,6 +456,24 @@ def main():
         gemm()
     torch.cuda.synchronize()
     assert torch.equal(y, y_ref), "raw entry points disagree with the wrappers"
+    # Settle: the GPU leaves its idle power state only after milliseconds of
+    # continuous work -- from idle the first ~20 ms of steps run up to 60 %
+    # slower, after which the step time holds steady (followed for 0.3 s) --
+    # and drops back into it during any pause (the first call of a torch
+    # kernel, such as the comparison above, can idle it for ~0.1 s).  So after
+    # the W warm-up steps, untimed steps until --settle-ms have passed, and
+    # the K timed steps follow them with no pause.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while args.settle_ms > 0:
+        for _ in range(20):
+            quant()
+            gemm()
+        settle_steps += 20
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t_settle) * 1e3 >= args.settle_ms:
+            break
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
 
     K_steps = args.steps
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -511,6 +532,7 @@ def main():
         "n_gpus": 1,
         "steps": K_steps,
         "warmup": args.warmup,
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
