@@ -1,5 +1,6 @@
-"""bench.py on the CPU: the multi-GPU refusal, and a static check that every
-name its functions read is bound (the GPU paths cannot run here)."""
+"""bench.py on the CPU: the multi-GPU refusal, the settle option, and a static
+check that every name its functions read is bound (the GPU paths cannot run
+here)."""
 import ast
 import builtins
 import os
@@ -14,6 +15,12 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, BENCH, "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_settle_option_is_offered():
+    r = subprocess.run([sys.executable, BENCH, "--help"], capture_output=True, text=True)
+    assert r.returncode == 0
+    assert "--settle-ms" in r.stdout
 
 
 def _bound_names(fn):
