@@ -198,7 +198,8 @@ def suite(reps):
     and quantize + GEMM of the per-channel M=128 and M=4096 shapes, are also
     run cold (a 1 GiB buffer written before every call, so inputs come from
     HBM rather than the 256 MB Infinity Cache); run under
-    `rocprofv3 --kernel-trace` for those per-dispatch durations."""
+    `rocprofv3 --kernel-trace` for those per-dispatch durations.  Each
+    back-to-back timing follows 25 ms of untimed calls of the same kernel."""
     import numpy as np
     import torch
 
@@ -217,6 +218,13 @@ def suite(reps):
     def b2b(fn):
         fn()
         torch.cuda.synchronize()
+        # settle first (the GPU runs slowly for tens of ms after a pause):
+        # batches of 50 calls until 25 ms have passed
+        t_s = time.perf_counter()
+        while time.perf_counter() - t_s < 0.025:
+            for _ in range(50):
+                fn()
+            torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(st)
         for _ in range(reps):
