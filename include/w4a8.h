@@ -134,7 +134,10 @@ w4a8_status_t w8a8_gemm_pg(const int8_t *xq, const float *x_scale, const int8_t 
  *     y[m, n] = fp16( x_scale[m] * sum_g P_g[m,n] * w_scale[n,g] ),
  *     P_g[m, n] = sum over k in group g of xq[m,k] * w4code[n,k]
  * xq int8 [M, K] with per-token x_scale fp32 [M]; w4 uint8 [N, K/2] (layout
- * above) with w_scale fp32 [N, K/gs]; group_size 64 or 128; K % 64 == 0. */
+ * above) with w_scale fp32 [N, K/gs]; group_size 64 or 128; K % 64 == 0.
+ * For 1 <= M <= 4 with M*K <= 65536 the product runs as a matrix-vector form
+ * that streams whole packed rows (same sums; the fp32 group terms are added in
+ * another order, within the same summation bound). */
 w4a8_status_t w4a8_gemm(const int8_t *xq, const float *x_scale, const uint8_t *w4,
                         const float *w_scale, int32_t group_size, w4a8_f16 *y, int64_t M,
                         int64_t N, int64_t K, w4a8_stream_t stream);

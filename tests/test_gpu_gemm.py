@@ -94,8 +94,15 @@ def test_gemm_pg(torch_gpu, oracle, M, N, K, gs):
     assert_fp16_close(host(y), y_ref, t_ref, G, what="fp16 y")
 
 
+# 1-4 tokens take the W4A8 matrix-vector form: 4, 8 and 16 chunks per lane
+# (one pass, or several over a row), N ragged against 16 rows per workgroup,
+# M * K at 65536 and just above it (the GEMM again)
+W4_FEW_SHAPES = [(1, 1001, 1024), (2, 333, 2048), (4, 4099, 4096), (3, 6144, 4096),
+                 (2, 257, 12288), (4, 100, 16384), (4, 129, 16512)]
+
+
 @pytest.mark.parametrize("gs", [64, 128])
-@pytest.mark.parametrize("M,N,K", PG_SHAPES)
+@pytest.mark.parametrize("M,N,K", PG_SHAPES + W4_FEW_SHAPES)
 def test_gemm_w4a8(torch_gpu, oracle, M, N, K, gs):
     import w4a8_int8_gemm_amd as w
     if K % gs:

@@ -36,8 +36,8 @@ constexpr int64_t kMaxKMv = 32768;            // the token's codes are staged in
 constexpr int64_t kMaxKWoMv = 16384;          // weight-only decode: the token as fp32 in LDS
 constexpr int64_t kMaxKGemm = int64_t(1) << 22; // a 256-row tile of K bytes stays below 2^30
 constexpr int64_t kMaxTiles = 0x7fffffff;     // 32 x 128 output tiles
-// Few-token per-channel product (the weight rows streamed whole): up to 4
-// tokens, whose codes are staged in LDS
+// Few-token per-channel and W4A8 products (the weight rows streamed whole): up
+// to 4 tokens, whose codes are staged in LDS
 constexpr int64_t kMaxMFew = 4;
 constexpr int64_t kMaxFewCodes = 65536;       // M * K bytes
 
@@ -228,6 +228,24 @@ w4a8_status_t run_pc(const char *fn, const int8_t *xq, const float *xs, const in
     return run_gemm(fn, GemmMode::PC, make_args(xq, xs, wq, sw, y, M, N, K, 0), stream);
 }
 
+// The W4A8 product on checked arguments: up to four tokens as the few-token
+// matrix-vector form, else the GEMM.
+w4a8_status_t run_w4(const char *fn, const int8_t *xq, const float *xs, const uint8_t *w4,
+                     const float *sw, int gs, w4a8_f16 *y, int64_t M, int64_t N, int64_t K,
+                     w4a8_stream_t stream)
+{
+    if (M >= 1 && M <= kMaxMFew && M * K <= kMaxFewCodes) {
+        if (N == 0)
+            return ok();
+        w4a8_status_t st = check_device();
+        if (st != W4A8_OK)
+            return st;
+        launch_few_w4(xq, xs, w4, sw, gs, y, (int)M, (int)N, (int)K, (hipStream_t)stream);
+        return check_launch(fn);
+    }
+    return run_gemm(fn, GemmMode::W4, make_args(xq, xs, w4, sw, y, M, N, K, gs), stream);
+}
+
 w4a8_status_t run_quant(const char *fn, const uint16_t *x, int64_t rows, int64_t K, int gs,
                         float qmax, void *q, float *scale, bool int4, w4a8_stream_t stream)
 {
@@ -321,8 +339,7 @@ w4a8_status_t w4a8_gemm(const int8_t *xq, const float *x_scale, const uint8_t *w
                                   true, true);
     if (st != W4A8_OK)
         return st;
-    return run_gemm("w4a8_gemm", GemmMode::W4,
-                    make_args(xq, x_scale, w4, w_scale, y, M, N, K, group_size), stream);
+    return run_w4("w4a8_gemm", xq, x_scale, w4, w_scale, group_size, y, M, N, K, stream);
 }
 
 w4a8_status_t int8_mv(const w4a8_f16 *x, const int8_t *wq, const float *w_scale, w4a8_f16 *y,
@@ -442,8 +459,8 @@ w4a8_status_t linear(w4a8_mode_t mode, const w4a8_f16 *x, int64_t M, int64_t K, 
         return run_gemm("linear", GemmMode::PG,
                         make_args(xq, xs, w, w_scale, y, M, N, K, group_size), stream);
     default:
-        return run_gemm("linear", GemmMode::W4,
-                        make_args(xq, xs, w, w_scale, y, M, N, K, group_size), stream);
+        return run_w4("linear", xq, xs, static_cast<const uint8_t *>(w), w_scale, group_size, y, M,
+                      N, K, stream);
     }
 }
 

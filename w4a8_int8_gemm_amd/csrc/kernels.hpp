@@ -43,6 +43,12 @@ void launch_gemm(GemmMode mode, const GemmArgs &a, hipStream_t st);
 void launch_few_pc(const int8_t *xq, const float *xs, const int8_t *w, const float *sw,
                    uint16_t *y, int M, int N, int K, hipStream_t st);
 
+// Few-token W4A8 product (1 <= M <= 4, M * K <= 64 KiB, gs 64 or 128): packed
+// int4 rows streamed whole against the tokens' codes in LDS; same results as
+// the W4A8 GEMM up to the fp32 summation order over the groups.
+void launch_few_w4(const int8_t *xq, const float *xs, const uint8_t *w, const float *sw, int gs,
+                   uint16_t *y, int M, int N, int K, hipStream_t st);
+
 // Decode matrix-vector: quantize the token, y[n] = rescale(sum_k q[k] w[n,k]).
 void launch_int8_mv(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, int N,
                     int K, int8_t *xq_out, float *xs_out, hipStream_t st);

@@ -485,6 +485,141 @@ void launch_few(const int8_t *xq, const float *xs, const int8_t *w, const float 
                        xq, xs, w, sw, y, M, N, K);
 }
 
+// Few tokens, W4A8: the decode kernel's int4 row streaming (16 lanes per row;
+// a 16-byte chunk holds 32 codes of one group) for M <= MT tokens quantized
+// per token.  The tokens' codes are staged in LDS split into even and odd k,
+// the order of the low and high nibbles of each weight byte; a nibble moved
+// into the high half of its byte reads as 16 * code, so each group's int32
+// dot product is 16 P_g, summed over the group's lanes and folded in fp32 by
+// its first lane with the group's weight scale; the row's lanes then add
+// their accumulators, and the 16 is undone with the token's scale (exact).
+template <int MT, int GS, int CPL>
+__global__ __launch_bounds__(256) void few_w4_kernel(const int8_t *__restrict__ xq,
+                                                     const float *__restrict__ xs,
+                                                     const uint8_t *__restrict__ w,
+                                                     const float *__restrict__ sw,
+                                                     uint16_t *__restrict__ y, int M, int N, int K)
+{
+    extern __shared__ __attribute__((aligned(16))) int8_t xq_s[];   // M * K bytes
+    constexpr int LPR = 16, RPB = 256 / LPR;
+    constexpr int CPG = GS / 32;                    // chunks per group
+    static_assert(CPG == 2 || CPG == 4, "chunks per group");
+    const int G = K / GS;
+    const int tid = threadIdx.x;
+    const int n = blockIdx.x * RPB + tid / LPR;
+    const int lr = tid % LPR;
+    const int nch = K >> 5;                         // 16-byte chunks per packed row
+    const uint4 *wr = reinterpret_cast<const uint4 *>(w + (int64_t)min(n, N - 1) * (K / 2));
+    const float *swr = sw + (int64_t)min(n, N - 1) * G;
+    const bool leader = lr % CPG == 0;
+
+    uint4 wv[CPL];
+    float swv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lr + LPR * j;
+        wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lr + LPR * j;
+        swv[j] = (leader && c < nch) ? swr[c / CPG] : 0.0f;
+    }
+    // the tokens' codes, 8 k at a time: (even k, odd k)
+    const int x8 = (M * K) >> 3;
+    for (int c = tid; c < x8; c += 256) {
+        const uint2 q = reinterpret_cast<const uint2 *>(xq)[c];
+        reinterpret_cast<uint2 *>(xq_s)[c] =
+            make_uint2(__builtin_amdgcn_perm(q.y, q.x, 0x06040200u),
+                       __builtin_amdgcn_perm(q.y, q.x, 0x07050301u));
+    }
+    __syncthreads();
+
+    float acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        acc[t] = 0.0f;
+    for (int base = 0;; base += LPR * CPL) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = base + lr + LPR * j;
+            const uint32_t wd[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                if (t < M) {
+                    int p = 0;
+                    if (c < nch) {
+                        const int8_t *xt = xq_s + t * K + c * 32;
+                        const uint4 q0 = *reinterpret_cast<const uint4 *>(xt);
+                        const uint4 q1 = *reinterpret_cast<const uint4 *>(xt + 16);
+                        const uint32_t qe[4] = {q0.x, q0.z, q1.x, q1.z};
+                        const uint32_t qo[4] = {q0.y, q0.w, q1.y, q1.w};
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            p = __builtin_amdgcn_sdot4((int)((wd[d] << 4) & 0xf0f0f0f0u), (int)qe[d], p, false);
+                            p = __builtin_amdgcn_sdot4((int)(wd[d] & 0xf0f0f0f0u), (int)qo[d], p, false);
+                        }
+                    }
+                    p = group_sum_i32<CPG>(p);      // every lane of the wave takes part
+                    if (leader && c < nch)
+                        acc[t] = fmaf((float)p, swv[j], acc[t]);
+                }
+            }
+        }
+        const int next = base + LPR * CPL;
+        if (next >= nch)
+            break;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = next + lr + LPR * j;
+            wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = next + lr + LPR * j;
+            swv[j] = (leader && c < nch) ? swr[c / CPG] : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t < M) {
+            const float a = group_sum_f32<LPR>(acc[t]);
+            if (lr == 0 && n < N)
+                y[(int64_t)t * N + n] = f2h(a * (xs[t] * 0.0625f));
+        }
+    }
+}
+
+template <int MT, int GS>
+void launch_few_w4_m(const int8_t *xq, const float *xs, const uint8_t *w, const float *sw,
+                     uint16_t *y, int M, int N, int K, hipStream_t st)
+{
+    const unsigned blocks = (unsigned)((N + 15) / 16);
+    const size_t lds = (size_t)M * K;
+    const int nch = K / 32;
+    if (nch <= 64)
+        hipLaunchKernelGGL((few_w4_kernel<MT, GS, 4>), dim3(blocks), dim3(256), lds, st, xq, xs, w,
+                           sw, y, M, N, K);
+    else if (nch <= 128)
+        hipLaunchKernelGGL((few_w4_kernel<MT, GS, 8>), dim3(blocks), dim3(256), lds, st, xq, xs, w,
+                           sw, y, M, N, K);
+    else
+        hipLaunchKernelGGL((few_w4_kernel<MT, GS, 16>), dim3(blocks), dim3(256), lds, st, xq, xs,
+                           w, sw, y, M, N, K);
+}
+
+template <int GS>
+void launch_few_w4_gs(const int8_t *xq, const float *xs, const uint8_t *w, const float *sw,
+                      uint16_t *y, int M, int N, int K, hipStream_t st)
+{
+    if (M <= 1)
+        launch_few_w4_m<1, GS>(xq, xs, w, sw, y, M, N, K, st);
+    else if (M <= 2)
+        launch_few_w4_m<2, GS>(xq, xs, w, sw, y, M, N, K, st);
+    else
+        launch_few_w4_m<4, GS>(xq, xs, w, sw, y, M, N, K, st);
+}
+
 template <int MT>
 void launch_few_m(const int8_t *xq, const float *xs, const int8_t *w, const float *sw, uint16_t *y,
                   int M, int N, int K, hipStream_t st)
@@ -513,6 +648,15 @@ void launch_few_pc(const int8_t *xq, const float *xs, const int8_t *w, const flo
         launch_few_m<2>(xq, xs, w, sw, y, M, N, K, st);
     else
         launch_few_m<4>(xq, xs, w, sw, y, M, N, K, st);
+}
+
+void launch_few_w4(const int8_t *xq, const float *xs, const uint8_t *w, const float *sw, int gs,
+                   uint16_t *y, int M, int N, int K, hipStream_t st)
+{
+    if (gs == 64)
+        launch_few_w4_gs<64>(xq, xs, w, sw, y, M, N, K, st);
+    else
+        launch_few_w4_gs<128>(xq, xs, w, sw, y, M, N, K, st);
 }
 
 void launch_mv_group(bool int4, int gs, const uint16_t *x, const uint8_t *w, const float *sw,
