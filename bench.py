@@ -92,9 +92,10 @@ def kernel_sample():
     HBM-bound kernels: quantize_act per token (4096x2560) and per group
     (4096x4096, gs 128 and 64), and the decode matrix-vector kernels
     (int8_mv 10240x2560, w8a8_mv_pg 14336x4096 gs=128, w4a8_mv 24576x4096),
-    and the few-token per-channel product (w8a8_gemm_pc at M = 2 and 4,
-    10240x2560), each three times with a 1 GiB buffer written before every
-    call so the weights come from HBM.  Meant to run under `rocprofv3 --pmc`
+    and the few-token per-channel and W4A8 products (w8a8_gemm_pc at M = 2
+    and 4, 10240x2560; w4a8_gemm gs=128 at M = 2 and 4, 24576x4096), each
+    three times with a 1 GiB buffer written before every call so the
+    weights come from HBM.  Meant to run under `rocprofv3 --pmc`
     (a few dispatches per kernel)."""
     import torch
 
@@ -173,6 +174,21 @@ def kernel_sample():
         for _ in range(3):
             flush.fill_(1)
             w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y), M, N, K, sp))
+        torch.cuda.synchronize()
+        del x, xq, xs, y
+    del wq, sw
+    N, K, gs = 24576, 4096, 128
+    wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
+    wq, sw = w.pack_weight_int4(wt, gs)
+    del wt
+    for M in (2, 4):
+        log(f"kernel sample: few-token W4A8 M={M} N={N} K={K} gs={gs}")
+        x = torch.from_numpy(synth.activations(M, K, seed=1)).cuda()
+        xq, xs = w.quantize_act(x, 0)
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        for _ in range(3):
+            flush.fill_(1)
+            w.check(L.w4a8_gemm(ptr(xq), ptr(xs), ptr(wq), ptr(sw), gs, ptr(y), M, N, K, sp))
         torch.cuda.synchronize()
         del x, xq, xs, y
     del wq, sw
