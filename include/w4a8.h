@@ -182,7 +182,9 @@ size_t linear_workspace_size(w4a8_mode_t mode, int64_t M, int64_t K, int32_t gro
 
 /* The whole layer with path selection ([P2] path selection): M == 1 runs the
  * mode's matrix-vector kernel (int8_mv, w8a8_mv_pg or w4a8_mv; K <= 32768);
- * otherwise quantize_act then the mode's GEMM.  What linear accepts does not depend on M: the GEMM's rules.
+ * otherwise quantize_act then the mode's product (w8a8_gemm_pc, w8a8_gemm_pg or
+ * w4a8_gemm, which themselves stream whole weight rows for up to four tokens).
+ * What linear accepts does not depend on M: the GEMM's rules.
  * x fp16 [M, K]; w is int8 [N, K] (PC, PG) or packed uint8 [N, K/2] (W4A8);
  * w_scale as the mode's GEMM takes it; group_size is ignored in PC mode.
  * workspace: device buffer of at least linear_workspace_size() bytes, 256-byte
