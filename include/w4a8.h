@@ -30,8 +30,10 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller, row-major
- *    with K contiguous, 16-byte aligned.  The library allocates no device
- *    memory.  fp16 data is passed as IEEE binary16 bit patterns (w4a8_f16).
+ *    with K contiguous.  Activations, codes, weights and outputs must be
+ *    16-byte aligned; fp32 scale vectors 4-byte aligned.  The library
+ *    allocates no device memory.  fp16 data is passed as IEEE binary16 bit
+ *    patterns (w4a8_f16).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work and return; results are ready when the stream is.
  *    Argument errors return before anything is enqueued; a kernel fault
@@ -62,7 +64,7 @@ typedef enum {
     W4A8_ERR_INVALID_ARG = 1, /* null pointer for a non-empty tensor, negative size, bad mode */
     W4A8_ERR_SHAPE = 2,       /* K not a multiple of what the kernel needs, bad group size,
                                  K so large that an int32 sum could overflow */
-    W4A8_ERR_ALIGNMENT = 3,   /* a tensor base pointer not 16-byte aligned */
+    W4A8_ERR_ALIGNMENT = 3,   /* a tensor base pointer not 16-byte aligned (scales: 4-byte) */
     W4A8_ERR_DEVICE = 4,      /* the current HIP device is not gfx950, or no device */
     W4A8_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch */
     W4A8_ERR_WORKSPACE = 6    /* workspace missing or smaller than linear_workspace_size() */
@@ -212,6 +214,33 @@ w4a8_status_t w8a8_gemm_pg_partials(const int8_t *xq, const int8_t *wq, int32_t 
 w4a8_status_t w4a8_gemm_partials(const int8_t *xq, const uint8_t *w4, int32_t group_size,
                                  int32_t *p, int64_t M, int64_t N, int64_t K,
                                  w4a8_stream_t stream);
+
+/* --------------------------------------------------------------------------
+ * Which kernel configuration a GEMM entry point runs (introspection: tests
+ * assert the configuration their shapes exercise; callers can log it).
+ * ------------------------------------------------------------------------ */
+typedef enum {
+    W4A8_OP_GEMM_PC = 0,       /* w8a8_gemm_pc */
+    W4A8_OP_GEMM_PG = 1,       /* w8a8_gemm_pg */
+    W4A8_OP_GEMM_W4A8 = 2,     /* w4a8_gemm */
+    W4A8_OP_GEMM_I32 = 3,      /* w8a8_gemm_i32 */
+    W4A8_OP_PG_PARTIALS = 4,   /* w8a8_gemm_pg_partials */
+    W4A8_OP_W4A8_PARTIALS = 5  /* w4a8_gemm_partials */
+} w4a8_gemm_op_t;
+
+/* For a call of `op` with these sizes on the current device, writes
+ *   out[0] = rows of the output tile a workgroup computes (0: the call runs
+ *            the few-token matrix-vector form instead of the tiled GEMM),
+ *   out[1] = columns of that tile,
+ *   out[2] = wavefronts per workgroup,
+ *   out[3] = workgroups launched (the grid is persistent: at most as many as
+ *            the device holds at once; each walks its share of the tiles),
+ *   out[4] = tiles of the M x N output,
+ *   out[5] = workgroups the device holds at once per compute unit.
+ * Argument rules and errors are those of the entry point itself; nothing is
+ * launched.  out is a host array of 6 int64_t. */
+w4a8_status_t gemm_tile_config(w4a8_gemm_op_t op, int64_t M, int64_t N, int64_t K,
+                               int32_t group_size, int64_t *out);
 
 /* --------------------------------------------------------------------------
  * Weight-only int8 comparison GEMM (W8A16): the baseline of the "cider"

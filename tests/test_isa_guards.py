@@ -4,8 +4,9 @@ The direct-to-LDS copies write M0 from inline asm without restoring it, which
 is only sound while nothing else in those kernels reads or writes M0: the
 compiler cannot be told about the write.  Copies that share one M0 value rely
 on no branch or label between the write and the load.  This test compiles
-gemm.hip to device assembly and fails on any M0 access outside the copies'
-asm blocks and on any copy not preceded by an M0 write in its basic block."""
+gemm.hip and gemm_pc.hip to device assembly and fails on any M0 access
+outside the copies' asm blocks and on any copy not preceded by an M0 write in
+its basic block."""
 import os
 import sys
 import re
@@ -24,16 +25,20 @@ from w4a8_int8_gemm_amd.build import FLAGS  # noqa: E402  (plain list; imports n
 def gemm_asm(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = str(tmp_path_factory.mktemp("isa") / "gemm.s")
+    d = tmp_path_factory.mktemp("isa")
     # the library's own device flags, so the checked code is the shipped code
     flags = [f for f in FLAGS if f != "-fPIC"]
-    cmd = [HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm.hip"), "-o", out]
-    subprocess.run(cmd, check=True, capture_output=True)
-    return open(out).read()
+    text = []
+    for src in ("gemm.hip", "gemm_pc.hip"):
+        out = str(d / (src + ".s"))
+        cmd = [HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+        subprocess.run(cmd, check=True, capture_output=True)
+        text.append(open(out).read())
+    return "\n".join(text)
 
 
 def _kernels(asm):
-    names = re.findall(r"^(_Z\S*gemm_kernel\S*):", asm, flags=re.M)
+    names = re.findall(r"^(_Z\S*gemm\w*_kernel\S*):", asm, flags=re.M)
     for n in names:
         i = asm.index(n + ":")
         yield n, asm[i:asm.index(".Lfunc_end", i)]

@@ -39,6 +39,7 @@ _SIGNATURES = {
     "w4a8_gemm_partials": [_vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp],
     "w8a16_gemm": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "w4a16_gemm": [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp],
+    "gemm_tile_config": [ctypes.c_int, _i64, _i64, _i64, _i32, ctypes.POINTER(_i64)],
 }
 _RESTYPES = {
     "w4a8_is_available": ctypes.c_int,
@@ -62,6 +63,15 @@ class Mode(enum.IntEnum):
     W8A8_PC = 0
     W8A8_PG = 1
     W4A8 = 2
+
+
+class GemmOp(enum.IntEnum):
+    GEMM_PC = 0
+    GEMM_PG = 1
+    GEMM_W4A8 = 2
+    GEMM_I32 = 3
+    PG_PARTIALS = 4
+    W4A8_PARTIALS = 5
 
 
 class W4A8Error(RuntimeError):

@@ -499,8 +499,6 @@ w4a8_status_t w4a8_gemm_partials(const int8_t *xq, const uint8_t *w4, int32_t gr
                     make_args(xq, nullptr, w4, nullptr, p, M, N, K, group_size), stream);
 }
 
-}  // extern "C"
-
 w4a8_status_t w8a16_gemm(const w4a8_f16 *x, const int8_t *wq, const float *w_scale, w4a8_f16 *y,
                          int64_t M, int64_t N, int64_t K, w4a8_stream_t stream)
 {
@@ -563,3 +561,52 @@ w4a8_status_t w4a16_gemm(const w4a8_f16 *x, const uint8_t *w4, const float *w_sc
                      reinterpret_cast<uint16_t *>(y), (int)M, (int)N, (int)K, (hipStream_t)stream);
     return check_launch(fn);
 }
+
+w4a8_status_t gemm_tile_config(w4a8_gemm_op_t op, int64_t M, int64_t N, int64_t K,
+                               int32_t group_size, int64_t *out)
+{
+    const char *fn = "gemm_tile_config";
+    if (!out)
+        return fail(W4A8_ERR_INVALID_ARG, "%s: null out", fn);
+    GemmMode mode;
+    bool pergroup = true, few = false;
+    switch (op) {
+    case W4A8_OP_GEMM_PC: mode = GemmMode::PC; pergroup = false; few = true; break;
+    case W4A8_OP_GEMM_I32: mode = GemmMode::I32; pergroup = false; break;
+    case W4A8_OP_GEMM_PG: mode = GemmMode::PG; break;
+    case W4A8_OP_PG_PARTIALS: mode = GemmMode::PG_PARTIALS; break;
+    case W4A8_OP_GEMM_W4A8: mode = GemmMode::W4; few = true; break;
+    case W4A8_OP_W4A8_PARTIALS: mode = GemmMode::W4_PARTIALS; break;
+    default: return fail(W4A8_ERR_INVALID_ARG, "%s: unknown op %d", fn, (int)op);
+    }
+    // the entry point's own shape rules (pointers are not inspected)
+    static const int8_t dummy[16] __attribute__((aligned(16))) = {0};
+    const float *fs = reinterpret_cast<const float *>(dummy);
+    w4a8_status_t st = check_gemm(fn, dummy, dummy, dummy, fs, fs, M, N, K,
+                                  pergroup ? group_size : 0, pergroup, false);
+    if (st != W4A8_OK)
+        return st;
+    for (int i = 0; i < 6; ++i)
+        out[i] = 0;
+    if (M == 0 || N == 0)
+        return ok();
+    int num_cu = 0;
+    st = check_device(&num_cu);
+    if (st != W4A8_OK)
+        return st;
+    if (few && M >= 1 && M <= kMaxMFew && M * K <= kMaxFewCodes)
+        return ok();                              // the few-token matrix-vector form
+    GemmArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K,
+                           pergroup ? group_size : 0);
+    a.num_cu = num_cu;
+    const TileInfo t = gemm_info(mode, a);
+    out[0] = t.bm;
+    out[1] = t.bn;
+    out[2] = t.waves;
+    out[3] = t.grid;
+    out[4] = t.tiles;
+    out[5] = t.per_cu;
+    return ok();
+}
+
+}  // extern "C"

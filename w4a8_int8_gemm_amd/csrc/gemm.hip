@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "kernels.hpp"
+#include "lds_copy.hpp"
 
 namespace w4a8 {
 
@@ -89,25 +90,6 @@ __device__ __forceinline__ uint32_t pair_rows_to_cols(uint32_t p, uint32_t sel)
     return __builtin_amdgcn_perm(p, q, sel);
 }
 
-// Swap lanes 32-63 of x with lanes 0-31 of y (v_permlane32_swap): lane l < 32
-// keeps x and receives y of lane l + 32 in y; lane l + 32 receives x of lane l
-// in x and keeps y.
-__device__ __forceinline__ void lane_half_swap(uint32_t &x, uint32_t &y)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
-    x = r[0];
-    y = r[1];
-}
-
-// Workgroup barrier that orders LDS accesses only: global loads stay in
-// flight across it (a full __syncthreads would also wait for them).
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 template <GemmMode MODE> struct ModeTraits {
     static constexpr bool int4 = (MODE == GemmMode::W4 || MODE == GemmMode::W4_PARTIALS);
     static constexpr bool pergroup = (MODE == GemmMode::PG || MODE == GemmMode::PG_PARTIALS ||
@@ -119,69 +101,6 @@ template <GemmMode MODE> struct ModeTraits {
     // weights as the MFMA's first operand: lane = output row, runs along n
     static constexpr bool nmajor = (MODE == GemmMode::PC);
 };
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Direct-to-LDS copies: each lane's bytes from global memory land at
-// M0 + size * lane.  Issued through asm so that the only waits on them are
-// the kernel's own (vmcnt before the barrier that publishes a stage); the
-// "memory" clobber keeps other memory accesses from moving across them.  One
-// wait state separates the SALU write of M0 from the load that reads it (a
-// gfx9 hazard).  M0 is not restored: nothing else in these kernels uses it
-// (the compiler cannot be told that asm writes M0, so a CPU test checks the
-// kernels' assembly for any other M0 access).
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const lds_void *)p;
-}
-__device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :
-                 : "s"(lds), "v"(src)
-                 : "memory");
-}
-
-// s_waitcnt that waits for the vector-memory counter only (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maximum).
-template <int N> __device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Buffer resource of a raw byte range [base, base + bytes): loads at offsets
-// past `bytes` return zeros instead of touching memory.
-__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    v4i r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));   // stride 0
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = 0x00020000;                                  // gfx9 raw buffer: 32-bit data format
-    return r;
-}
-
-// M0 = the LDS address the next direct-to-LDS buffer loads write at.
-__device__ __forceinline__ void set_m0(uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" : : "s"(lds) : "memory");
-}
-
-// 16 bytes per lane from a buffer resource into LDS at M0 + OFF + 16 * lane,
-// from byte offset voff + OFF (+ soff) of the resource.  The immediate OFF
-// adds to both addresses and takes part in the range check: lanes whose
-// voff + OFF lies past the resource's size read zeros.  M0 must hold the
-// LDS base (set_m0); nothing else in these kernels touches M0.
-template <int OFF>
-__device__ __forceinline__ void copy16_buf_to_lds(v4i rsrc, uint32_t voff, uint32_t soff)
-{
-    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
-                 :
-                 : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF)
-                 : "memory");
-}
 
 // Persistent kernel: the grid holds at most as many workgroups as fit on the
 // device at once, and workgroup b computes the tiles b', b' + G, b' + 2G, ...
@@ -937,104 +856,213 @@ void launch_cfg(const GemmArgs &a, hipStream_t st)
                        a, tiles_m, tiles_n, group_m);
 }
 
+// Tile shapes choose_tile can return for a mode (only these are compiled).
+template <GemmMode MODE, int GS> constexpr bool tile_ok(TileShape t)
+{
+    using T = ModeTraits<MODE>;
+    constexpr bool pg64 = (MODE == GemmMode::PG || MODE == GemmMode::PG_PARTIALS) && GS == 64;
+    switch (t) {
+    case TileShape::T32x32: return !T::int4;
+    case TileShape::T32x128: return T::int4;
+    case TileShape::T64x64: return !T::pergroup;
+    case TileShape::T64x128: return true;
+    case TileShape::T128x128: return true;
+    case TileShape::T128x128w8: return pg64;
+    case TileShape::T256x128: return !T::pergroup;
+    case TileShape::T256x128w8: return T::pergroup && !pg64;
+    case TileShape::T256x160: return !T::pergroup;
+    case TileShape::T256x320w8: return false;       // a kernel of its own
+    }
+    return false;
+}
+
+// F<BM, BN, WM, WN, MODE, GS>::run(args...) for the runtime tile t.
+template <GemmMode MODE, int GS, template <int, int, int, int, GemmMode, int> class F, typename... A>
+int with_tile(TileShape t, A &&...args)
+{
+#define W4A8_TILE(S, BM, BN, WM, WN)                                                 \
+    case TileShape::S:                                                              \
+        if constexpr (tile_ok<MODE, GS>(TileShape::S))                              \
+            return F<BM, BN, WM, WN, MODE, GS>::run(args...);                       \
+        return -1;
+    switch (t) {
+        W4A8_TILE(T32x32, 32, 32, 1, 1)
+        W4A8_TILE(T32x128, 32, 128, 1, 4)
+        W4A8_TILE(T64x64, 64, 64, 1, 2)
+        W4A8_TILE(T64x128, 64, 128, 2, 2)
+        W4A8_TILE(T128x128, 128, 128, 2, 2)
+        W4A8_TILE(T128x128w8, 128, 128, 2, 4)
+        W4A8_TILE(T256x128, 256, 128, 2, 2)
+        W4A8_TILE(T256x128w8, 256, 128, 4, 2)
+        W4A8_TILE(T256x160, 256, 160, 4, 1)
+    case TileShape::T256x320w8:
+        return -1;
+    }
+#undef W4A8_TILE
+    return -1;
+}
+
+template <int BM, int BN, int WM, int WN, GemmMode MODE, int GS> struct LaunchCfgF {
+    static int run(const GemmArgs &a, hipStream_t st)
+    {
+        launch_cfg<BM, BN, WM, WN, MODE, GS>(a, st);
+        return 0;
+    }
+};
+template <int BM, int BN, int WM, int WN, GemmMode MODE, int GS> struct OccF {
+    static int run() { return groups_per_cu<BM, BN, WM, WN, MODE, GS>(); }
+};
+
+template <GemmMode MODE, int GS>
+void launch_mode(const GemmArgs &a, hipStream_t st)
+{
+    const TileShape t = choose_tile(MODE, GS, a.M, a.N, a.K, a.num_cu);
+    if (t == TileShape::T256x320w8)
+        launch_gemm_pc2(MODE == GemmMode::I32, a, st, true);
+    else
+        with_tile<MODE, GS, LaunchCfgF>(t, a, st);
+}
+
+template <GemmMode MODE, int GS>
+int resident_groups(TileShape t)
+{
+    const int o = with_tile<MODE, GS, OccF>(t);
+    return o > 0 ? o : 1;
+}
+
+template <GemmMode MODE, int GS>
+TileInfo info_mode(const GemmArgs &a)
+{
+    const TileShape t = choose_tile(MODE, GS, a.M, a.N, a.K, a.num_cu);
+    if (t == TileShape::T256x320w8)
+        return launch_gemm_pc2(MODE == GemmMode::I32, a, nullptr, false);
+    TileInfo r = tile_dims(t);
+    const int64_t tiles = (int64_t)((a.M + r.bm - 1) / r.bm) * ((a.N + r.bn - 1) / r.bn);
+    r.per_cu = resident_groups<MODE, GS>(t);
+    const int64_t resident = (int64_t)a.num_cu * r.per_cu;
+    r.tiles = tiles;
+    r.grid = tiles < resident ? tiles : resident;
+    return r;
+}
+
+}  // namespace
+
 // Pick a tile shape: large tiles when the output is big, smaller ones when
 // too few tiles would leave compute units idle.  The per-group modes hold
 // fp32 accumulators next to the int32 ones, so their large tile is 256x128
 // with eight 64x64 waves (two per SIMD, which lets one wave's fold run beside
-// the other's MFMAs) rather than four larger ones.
-template <GemmMode MODE, int GS>
-void launch_mode(const GemmArgs &a, hipStream_t st)
+// the other's MFMAs) rather than four larger ones.  Each raw-sum export takes
+// exactly the tile of the product it checks (I32 that of PC, the partials
+// that of their per-group product).
+TileShape choose_tile(GemmMode mode, int gs, int M, int N, int K, int num_cu)
 {
-    constexpr bool pergroup = ModeTraits<MODE>::pergroup;
-    const int64_t t256x160 = (int64_t)((a.M + 255) / 256) * ((a.N + 159) / 160);
-    const int64_t t256x128 = (int64_t)((a.M + 255) / 256) * ((a.N + 127) / 128);
-    const int64_t t128x128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+    const bool pergroup = mode != GemmMode::PC && mode != GemmMode::I32;
+    const bool int4 = mode == GemmMode::W4 || mode == GemmMode::W4_PARTIALS;
+    const bool pg64 = (mode == GemmMode::PG || mode == GemmMode::PG_PARTIALS) && gs == 64;
+    const int64_t t256x160 = (int64_t)((M + 255) / 256) * ((N + 159) / 160);
+    const int64_t t256x128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
+    const int64_t t128x128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     // Few tokens: the weights are streamed once and the output is small, so
     // the tile count decides how many compute units pull weights.  32x32
     // single-wave tiles (int8 weights) and 64x64 ones (per-channel) give four
     // and two times the tiles of 32x128 / 64x128; the narrow tiles did not pay
     // for W4A8, nor for the per-group modes above 32 tokens.
-    if (a.M <= 32) {
-        if constexpr (ModeTraits<MODE>::int4)
-            launch_cfg<32, 128, 1, 4, MODE, GS>(a, st);
-        else
-            launch_cfg<32, 32, 1, 1, MODE, GS>(a, st);
-        return;
-    }
-    if (a.M <= 64) {
-        if constexpr (pergroup)
-            launch_cfg<64, 128, 2, 2, MODE, GS>(a, st);
-        else
-            launch_cfg<64, 64, 1, 2, MODE, GS>(a, st);
-        return;
-    }
-    if constexpr (!pergroup) {
+    if (M <= 32)
+        return int4 ? TileShape::T32x128 : TileShape::T32x32;
+    if (M <= 64)
+        return pergroup ? TileShape::T64x128 : TileShape::T64x64;
+    if (!pergroup) {
         // Large outputs: the cheapest of the three big tiles by (rounds of
         // tiles over the compute units) x (tile area / its measured relative
         // rate: 256x160 1, 256x128 0.9, 128x128 0.85), so that a last round
         // left mostly empty counts against a tile shape.
         if (t128x128 >= 256) {
-            const int64_t cu = a.num_cu > 0 ? a.num_cu : 1;
+            const int64_t cu = num_cu > 0 ? num_cu : 1;
             auto rounds = [&](int64_t t) { return (double)((t + cu - 1) / cu); };
-            const double c160 = a.N % 160 == 0 ? rounds(t256x160) * (256.0 * 160.0) : 1e300;
+            const double c160 = N % 160 == 0 ? rounds(t256x160) * (256.0 * 160.0) : 1e300;
             const double c256 = rounds(t256x128) * (256.0 * 128.0 / 0.9);
             const double c128 = rounds(t128x128) * (128.0 * 128.0 / 0.85);
             if (c160 <= c256 && c160 <= c128)
-                launch_cfg<256, 160, 4, 1, MODE, GS>(a, st);
-            else if (c256 <= c128)
-                launch_cfg<256, 128, 2, 2, MODE, GS>(a, st);
-            else
-                launch_cfg<128, 128, 2, 2, MODE, GS>(a, st);
-            return;
+                return (K % 128 == 0 && N % 320 == 0) ? TileShape::T256x320w8 : TileShape::T256x160;
+            if (c256 <= c128)
+                return TileShape::T256x128;
+            return TileShape::T128x128;
         }
     }
     // per-group gs=64 at 256x128 needs more than the 256 registers a wave
     // has at two waves per SIMD (it spills); it takes 128x128 below
-    if constexpr (pergroup && !(MODE == GemmMode::PG && GS == 64)) {
-        if (t256x128 >= 384) {             // two waves per SIMD: folds run beside MFMAs
-            launch_cfg<256, 128, 4, 2, MODE, GS>(a, st);
-            return;
-        }
-    }
+    if (pergroup && !pg64 && t256x128 >= 384)
+        return TileShape::T256x128w8;   // two waves per SIMD: folds run beside MFMAs
     // per-group gs=64 is bound by its fold (VALU): eight 64x32 waves (two per
     // SIMD, few registers) overlap one wave's fold with another's MFMAs; the
     // extra LDS reads of the narrower waves cost nothing at its MFMA rate
-    if constexpr (MODE == GemmMode::PG && GS == 64) {
-        if (t128x128 >= 256) {
-            launch_cfg<128, 128, 2, 4, MODE, GS>(a, st);
-            return;
-        }
-    }
-    if (t128x128 >= 256)
-        launch_cfg<128, 128, 2, 2, MODE, GS>(a, st);
-    else
-        launch_cfg<64, 128, 2, 2, MODE, GS>(a, st);
+    if (pg64 && t128x128 >= 256)
+        return TileShape::T128x128w8;
+    return t128x128 >= 256 ? TileShape::T128x128 : TileShape::T64x128;
 }
+
+TileInfo tile_dims(TileShape t)
+{
+    TileInfo r{};
+    switch (t) {
+    case TileShape::T32x32: r.bm = 32; r.bn = 32; r.waves = 1; break;
+    case TileShape::T32x128: r.bm = 32; r.bn = 128; r.waves = 4; break;
+    case TileShape::T64x64: r.bm = 64; r.bn = 64; r.waves = 2; break;
+    case TileShape::T64x128: r.bm = 64; r.bn = 128; r.waves = 4; break;
+    case TileShape::T128x128: r.bm = 128; r.bn = 128; r.waves = 4; break;
+    case TileShape::T128x128w8: r.bm = 128; r.bn = 128; r.waves = 8; break;
+    case TileShape::T256x128: r.bm = 256; r.bn = 128; r.waves = 4; break;
+    case TileShape::T256x128w8: r.bm = 256; r.bn = 128; r.waves = 8; break;
+    case TileShape::T256x160: r.bm = 256; r.bn = 160; r.waves = 4; break;
+    case TileShape::T256x320w8: r.bm = 256; r.bn = 320; r.waves = 8; break;
+    }
+    return r;
+}
+
+namespace {
+
+// Dispatch on the mode and group size (template arguments).
+template <template <GemmMode, int> class F, typename... A>
+auto by_mode(GemmMode mode, int gs, A &&...args)
+{
+    switch (mode) {
+    case GemmMode::PC: return F<GemmMode::PC, 0>::run(args...);
+    case GemmMode::I32: return F<GemmMode::I32, 0>::run(args...);
+    case GemmMode::PG:
+        return gs == 64 ? F<GemmMode::PG, 64>::run(args...) : F<GemmMode::PG, 128>::run(args...);
+    case GemmMode::PG_PARTIALS:
+        return gs == 64 ? F<GemmMode::PG_PARTIALS, 64>::run(args...)
+                        : F<GemmMode::PG_PARTIALS, 128>::run(args...);
+    case GemmMode::W4:
+        return gs == 64 ? F<GemmMode::W4, 64>::run(args...) : F<GemmMode::W4, 128>::run(args...);
+    case GemmMode::W4_PARTIALS:
+        return gs == 64 ? F<GemmMode::W4_PARTIALS, 64>::run(args...)
+                        : F<GemmMode::W4_PARTIALS, 128>::run(args...);
+    }
+    return F<GemmMode::PC, 0>::run(args...);
+}
+
+template <GemmMode MODE, int GS> struct LaunchF {
+    static int run(const GemmArgs &a, hipStream_t st)
+    {
+        launch_mode<MODE, GS>(a, st);
+        return 0;
+    }
+};
+template <GemmMode MODE, int GS> struct InfoF {
+    static TileInfo run(const GemmArgs &a) { return info_mode<MODE, GS>(a); }
+};
 
 }  // namespace
 
+TileInfo gemm_info(GemmMode mode, const GemmArgs &a)
+{
+    return by_mode<InfoF>(mode, a.gs, a);
+}
+
 void launch_gemm(GemmMode mode, const GemmArgs &a, hipStream_t st)
 {
-    switch (mode) {
-    case GemmMode::PC: launch_mode<GemmMode::PC, 0>(a, st); break;
-    case GemmMode::I32: launch_mode<GemmMode::I32, 0>(a, st); break;
-    case GemmMode::PG:
-        if (a.gs == 64) launch_mode<GemmMode::PG, 64>(a, st);
-        else launch_mode<GemmMode::PG, 128>(a, st);
-        break;
-    case GemmMode::PG_PARTIALS:
-        if (a.gs == 64) launch_mode<GemmMode::PG_PARTIALS, 64>(a, st);
-        else launch_mode<GemmMode::PG_PARTIALS, 128>(a, st);
-        break;
-    case GemmMode::W4:
-        if (a.gs == 64) launch_mode<GemmMode::W4, 64>(a, st);
-        else launch_mode<GemmMode::W4, 128>(a, st);
-        break;
-    case GemmMode::W4_PARTIALS:
-        if (a.gs == 64) launch_mode<GemmMode::W4_PARTIALS, 64>(a, st);
-        else launch_mode<GemmMode::W4_PARTIALS, 128>(a, st);
-        break;
-    }
+    by_mode<LaunchF>(mode, a.gs, a, st);
 }
 
 }  // namespace w4a8

@@ -37,6 +37,30 @@ struct GemmArgs {
 
 void launch_gemm(GemmMode mode, const GemmArgs &a, hipStream_t st);
 
+// Tile configurations of the GEMM kernel (BM x BN per workgroup; "w8" = eight
+// waves, i.e. two per SIMD, where the default is four).
+enum class TileShape : int {
+    T32x32, T32x128, T64x64, T64x128, T128x128, T128x128w8, T256x128, T256x128w8, T256x160,
+    T256x320w8   // the per-channel kernel of its own (K % 128 == 0)
+};
+struct TileInfo {
+    int bm, bn, waves;    // output tile per workgroup and its wavefronts
+    int64_t tiles;        // tiles of the M x N output
+    int64_t grid;         // workgroups launched (persistent: at most what fits at once)
+    int per_cu;           // workgroups a compute unit holds at once
+};
+// The tile a GEMM of this mode and size runs with on a device of num_cu
+// compute units (each raw-sum export takes its product's choice).
+TileShape choose_tile(GemmMode mode, int gs, int M, int N, int K, int num_cu);
+TileInfo tile_dims(TileShape t);
+// The tile and grid launch_gemm would use for these arguments.
+TileInfo gemm_info(GemmMode mode, const GemmArgs &a);
+
+// The per-channel (or raw int32, i32_out) GEMM on 256 x 320 tiles of eight
+// waves (K % 128 == 0); launches only when `launch`, and returns its tile and
+// grid either way.
+TileInfo launch_gemm_pc2(bool i32_out, const GemmArgs &a, hipStream_t st, bool launch);
+
 // Few-token per-channel product (1 <= M <= 4, M * K <= 64 KiB): the weight
 // rows streamed whole against the tokens' codes in LDS; equals the
 // per-channel GEMM bit for bit.

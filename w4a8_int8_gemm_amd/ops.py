@@ -10,7 +10,7 @@ import ctypes
 
 import torch
 
-from ._lib import Mode, check, lib
+from ._lib import GemmOp, Mode, check, lib
 
 
 def _need(t, dtype, name, ndim):
@@ -259,3 +259,13 @@ def w4a16_gemm(x, w4, w_scale, group_size: int, out=None):
     with torch.cuda.device(x.device):
         check(lib().w4a16_gemm(_p(x), _p(w4), _p(w_scale), group_size, _p(out), M, N, K, _st(x)))
     return out
+
+
+def gemm_tile_config(op, M: int, N: int, K: int, group_size: int = 0) -> dict:
+    """The kernel configuration a GEMM entry point runs for these sizes on the
+    current device (nothing is launched): tile rows and columns (bm == 0: the
+    few-token matrix-vector form), waves per workgroup, workgroups launched,
+    output tiles and workgroups per compute unit."""
+    out = (ctypes.c_int64 * 6)()
+    check(lib().gemm_tile_config(int(GemmOp(op)), M, N, K, group_size, out))
+    return dict(bm=out[0], bn=out[1], waves=out[2], grid=out[3], tiles=out[4], per_cu=out[5])
