@@ -54,6 +54,8 @@ def lib():
         L.oracle_f64_to_f16.argtypes = [ctypes.c_double]
         L.oracle_f64_to_f16.restype = ctypes.c_uint16
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         L.oracle_w8a16.argtypes = [_u16p, _i8p, _f32p, _i64, _i64, _i64, _u16p, _f64p]
         L.oracle_w8a16.restype = None
         L.oracle_w4a16.argtypes = [_u16p, _i8p, _f32p, _i64, _i64, _i64, _i64, _u16p, _f64p]
@@ -85,6 +87,11 @@ def _p(a: np.ndarray, typ):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops (timing: one core against all)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------------------- fp16 rounding

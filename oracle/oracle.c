@@ -104,6 +104,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Set that number (timing runs measure the oracle on one thread and on all). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* -------------------------------------------------------------------------
  * Symmetric quantization of fp16 rows ([P1] kernel design, steps 1-2;
  * [P2] modes table).  For each row r and each slice g of `glen` contiguous

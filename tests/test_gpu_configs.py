@@ -1,11 +1,22 @@
 """GPU parity at the benchmark workloads' full sizes, through linear() (the
 launch configuration the benchmark times).
 
-Activation and weight quantization are compared in full, bit for bit.  The
-fp16 outputs are compared on a sample of rows x columns that the oracle
-computes on the sampled sub-problem (per-token and per-channel/per-group
-quantization are row-local, so the sub-problem's codes are the full
-problem's codes); the per-channel int32 sums are compared on the same sample.
+Every output is compared, not a sample:
+
+* activation and weight quantization: codes and scales in full, bit for bit;
+* the layer's fp16 output: every element against the oracle within the fp16
+  tolerance (per-channel) or the tolerance plus the per-group summation
+  allowance; the oracle runs in bands of whole rows (per-token and per-group
+  quantization and the GEMM are row-local, so a band of rows is the same
+  sub-problem on both sides);
+* per-channel: every int32 sum of the same GEMM kernel (the raw-sum export runs
+  the product's tile configuration, asserted below), bit for bit;
+* per-group and W4A8: the int32 partial sums of the full-size launch (the
+  export takes the product's tile configuration, asserted) on whole-row bands
+  covering every column -- the first and the last tile row -- bit for bit.
+
+The oracle needs about a minute of host time for all shapes together on the
+GPU machine's cores.
 """
 import numpy as np
 import pytest
@@ -21,10 +32,23 @@ for name, wl in synth.WORKLOADS.items():
         CASES.append(pytest.param(wl["mode"], M, N, K, wl["gs"], wl["outliers"],
                                   id=f"{name}-{M}x{N}x{K}"))
 
+# rows of int32 partials (G x rows x N x 4 bytes) the oracle holds at a time
+_BAND_BYTES = 1 << 29
+
 
 @pytest.fixture(scope="module")
 def torch_gpu():
     return require_gpu()
+
+
+def _shape(cfg):
+    """The tile configuration proper (occupancy may differ between the builds
+    of one tile for different epilogues)."""
+    return cfg["bm"], cfg["bn"], cfg["waves"]
+
+
+def _bands(M, rows):
+    return [(a, min(M, a + rows)) for a in range(0, M, rows)]
 
 
 @pytest.mark.parametrize("mode,M,N,K,gs,outliers", CASES)
@@ -56,29 +80,44 @@ def test_workload_full_size(torch_gpu, oracle, mode, M, N, K, gs, outliers):
     assert_equal(host(xs), xso, "activation scales")
     assert_equal(host(xq), xo, "activation codes")
 
-    # the layer through linear()
-    m_idx = synth.sample_indices(M, 48, seed=M, salt=1)
-    n_idx = synth.sample_indices(N, 256, seed=N, salt=2)
-    y = w.linear({"pc": w.Mode.W8A8_PC, "pg": w.Mode.W8A8_PG, "w4a8": w.Mode.W4A8}[mode],
-                 xd, wg, swg, gs)
-    ys = host(y[torch.as_tensor(m_idx, device="cuda")][:, torch.as_tensor(n_idx, device="cuda")])
+    # the layer through linear(), every output
+    y = host(w.linear({"pc": w.Mode.W8A8_PC, "pg": w.Mode.W8A8_PG, "w4a8": w.Mode.W4A8}[mode],
+                      xd, wg, swg, gs))
+    del xd
+    if mode == "pc":
+        c = host(w.w8a8_gemm_i32(xq, wg)) if M > 1 else None
+        if M > 1:
+            tile = _shape(w.gemm_tile_config(w.GemmOp.GEMM_PC, M, N, K))
+            assert tile == _shape(w.gemm_tile_config(w.GemmOp.GEMM_I32, M, N, K)), tile
+        for a, b in _bands(M, 512):
+            c_ref = oracle.gemm_i32(xo[a:b], wcodes)
+            if c is not None:
+                assert_equal(c[a:b], c_ref, f"int32 sums, rows {a}..{b}")
+            y_ref = oracle.epilogue_pc(c_ref, xso[a:b], swo)
+            assert_fp16_close(y[a:b], y_ref, what=f"fp16 y, rows {a}..{b}")
+        return
+
+    G = K // gs
+    epi = oracle.epilogue_pg if mode == "pg" else oracle.epilogue_w4a8
+    rows = max(1, min(512, _BAND_BYTES // (G * N * 4)))
+    for a, b in _bands(M, rows):
+        p_ref = oracle.gemm_partials(xo[a:b], wcodes, gs)
+        y_ref, t = epi(p_ref, xso[a:b], swo)
+        assert_fp16_close(y[a:b], y_ref, t, G, what=f"fp16 y, rows {a}..{b}")
     del y
 
-    xs_sub, ws_sub = xo[m_idx], wcodes[n_idx]
-    if mode == "pc":
-        c = oracle.gemm_i32(xs_sub, ws_sub)
-        y_ref = oracle.epilogue_pc(c, xso[m_idx], swo[n_idx])
-        assert_fp16_close(ys, y_ref, what="fp16 y (sample)")
-        if M > 1:
-            cg = w.w8a8_gemm_i32(xq, wg)
-            cs = host(cg[torch.as_tensor(m_idx, device="cuda")][:, torch.as_tensor(n_idx, device="cuda")])
-            assert_equal(cs, c, "int32 sums (sample)")
-    elif mode == "pg":
-        p = oracle.gemm_partials(xs_sub, ws_sub, gs)
-        y_ref, t = oracle.epilogue_pg(p, xso[m_idx], swo[n_idx])
-        assert_fp16_close(ys, y_ref, t, K // gs, what="fp16 y (sample)")
-    else:
-        p = oracle.gemm_partials(xs_sub, ws_sub, gs)
-        y_ref, t = oracle.epilogue_w4a8(p, xso[m_idx], swo[n_idx])
-        assert_fp16_close(ys, y_ref, t, K // gs, what="fp16 y (sample)")
+    # int32 partials of the full-size launch, first and last tile rows
+    prod = w.GemmOp.GEMM_PG if mode == "pg" else w.GemmOp.GEMM_W4A8
+    part = w.GemmOp.PG_PARTIALS if mode == "pg" else w.GemmOp.W4A8_PARTIALS
+    tp = _shape(w.gemm_tile_config(part, M, N, K, gs))
+    assert tp == _shape(w.gemm_tile_config(prod, M, N, K, gs)), tp
+    bm = tp[0]
+    p = (w.w8a8_gemm_pg_partials(xq, wg, gs) if mode == "pg"
+         else w.w4a8_gemm_partials(xq, wg, gs))
+    last = ((M - 1) // bm) * bm
+    for a, b in ((0, bm), (last, M)):
+        got = host(p[:, a:b, :].contiguous())
+        assert_equal(got, oracle.gemm_partials(xo[a:b], wcodes, gs),
+                     f"int32 partials, tile rows {a}..{b}")
+    del p
     torch.cuda.empty_cache()

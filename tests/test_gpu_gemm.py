@@ -3,8 +3,10 @@ bit, fp16 outputs within tolerance, against the oracle on the same seeded
 int8 codes and scales (drawn by the input generator, not by either side).
 
 Shapes are chosen to exercise every tile configuration the library selects
-(64x64, 128x64, 128x128, 256x128, 256x160), ragged M/N edges, N not a multiple
-of 4 (scalar stores), and K with a half-filled last stage (K % 128 == 64)."""
+(32x32, 64x64, 64x128, 128x128, 256x128, 256x160, 256x320), ragged M/N edges,
+N not a multiple of 4 (scalar stores), and K with a half-filled last stage
+(K % 128 == 64); test_tile_selection asserts which configuration the large
+shapes run (gemm_tile_config)."""
 import numpy as np
 import pytest
 
@@ -31,6 +33,10 @@ PC_SHAPES = [
     (1500, 8196, 320), (1500, 8200, 1280),
     # 256x160 tiles, one round over the CUs, ragged M
     (1000, 10240, 256),
+    # 256x320 tiles of eight waves: two tiles per workgroup, 8 K-stages (the
+    # ring of two wraps four times per tile and the stage stream crosses
+    # tile boundaries); then a ragged last tile row (4000 = 15 * 256 + 160)
+    (4096, 10240, 1024), (4000, 10240, 640),
     # few tokens: 32x32 and 64x64 tiles, N ragged against them (scalar stores
     # where N % 8 != 0), a K tail; the M = 32 / 64 rows of the N=10240 K=2560
     # layer
@@ -46,6 +52,47 @@ PC_SHAPES = [
     (2, 1001, 1024), (4, 333, 2048), (3, 10240, 2560), (1, 4099, 4096), (4, 777, 16384),
     (2, 5, 32768), (4, 129, 16448), (3, 4099, 14336), (4, 4096, 12288),
 ]
+
+
+def _shape(cfg):
+    """The tile configuration proper (occupancy may differ between the builds
+    of one tile for different epilogues)."""
+    return cfg["bm"], cfg["bn"], cfg["waves"]
+
+
+# (M, N, K) -> (tile rows, tile columns, waves) of the per-channel GEMM and its
+# int32 export, for the shapes whose tile choice the tests rely on
+EXPECTED_TILES = {
+    (4096, 10240, 1024): (256, 320, 8),
+    (4000, 10240, 640): (256, 320, 8),
+    (4096, 10240, 2560): (256, 320, 8),
+    (8192, 10240, 2560): (256, 320, 8),
+    (1000, 10240, 256): (256, 160, 4),
+    (1024, 10240, 2560): (256, 160, 4),
+    (1500, 10240, 192): (256, 128, 4),     # K % 128 != 0; 2 rounds of 256x128 beat 256x160
+    (2000, 8200, 1024): (128, 128, 4),     # N % 160 != 0
+    (2048, 10240, 128): (256, 320, 8),     # one K-stage per tile
+}
+
+
+def test_tile_selection(torch_gpu):
+    import w4a8_int8_gemm_amd as w
+    for (M, N, K), want in EXPECTED_TILES.items():
+        t = w.gemm_tile_config(w.GemmOp.GEMM_PC, M, N, K)
+        assert _shape(t) == want, ((M, N, K), t)
+        assert _shape(w.gemm_tile_config(w.GemmOp.GEMM_I32, M, N, K)) == want, (M, N, K)
+    # two tiles per workgroup at 4096 x 10240 (256 compute units, one each)
+    t = w.gemm_tile_config(w.GemmOp.GEMM_PC, 4096, 10240, 1024)
+    assert t["tiles"] >= 2 * t["grid"], t
+    # every per-group and W4A8 raw-sum export takes its product's tile
+    for gs in (64, 128):
+        for (M, N, K) in [(1024, 4096, 256), (2048, 8192, 256), (1800, 6100, 384),
+                          (4096, 14336, 4096), (4516, 24576, 4096), (31, 1000, 384)]:
+            assert (_shape(w.gemm_tile_config(w.GemmOp.GEMM_PG, M, N, K, gs)) ==
+                    _shape(w.gemm_tile_config(w.GemmOp.PG_PARTIALS, M, N, K, gs))), (M, N, K, gs)
+            if M > 4:   # 1-4 tokens: the W4A8 product takes its matrix-vector form
+                assert (_shape(w.gemm_tile_config(w.GemmOp.GEMM_W4A8, M, N, K, gs)) ==
+                        _shape(w.gemm_tile_config(w.GemmOp.W4A8_PARTIALS, M, N, K, gs))), (M, N, K, gs)
 
 
 @pytest.mark.parametrize("M,N,K", PC_SHAPES)

@@ -27,11 +27,13 @@ def test_int8_mv(torch_gpu, oracle, N, K):
     assert_equal(host(xs), r["sa"], "token scale")
     assert_equal(host(xq), r["xq"][0], "token codes")
     assert_fp16_close(host(y), r["y"][0], what="fp16 y")
-    # bit-identical to the GEMM path at M = 1 (where the GEMM accepts K)
+    # bit-identical to quantize_act + w8a8_gemm_pc at M = 1 (where the GEMM
+    # accepts K), which runs the few-token form there; the comparison with
+    # the tiled GEMM itself is in test_gpu_few_token.py
     if K % 64 == 0:
         xq2, xs2 = w.quantize_act(dev(x))
         y2 = w.w8a8_gemm_pc(xq2, xs2, dev(wq), dev(sw))
-        assert_equal(host(y), host(y2)[0], "MV vs GEMM at M=1")
+        assert_equal(host(y), host(y2)[0], "MV vs w8a8_gemm_pc at M=1")
 
 
 def test_int8_mv_zero_token(torch_gpu, oracle):
@@ -58,9 +60,10 @@ def test_linear_pc_end_to_end(torch_gpu, oracle, M):
     assert_fp16_close(host(y), r["y"], what=f"linear pc M={M}")
     if M == 1:   # the dispatch picked the MV kernel: identical to calling it directly
         assert_equal(host(y)[0], host(w.int8_mv(dev(x[0]), wq_g, sw_g)), "dispatch to MV")
-    else:        # identical to quantize_act + w8a8_gemm_pc
+    else:        # identical to quantize_act + w8a8_gemm_pc (few-token form at M <= 4)
         xq, xs = w.quantize_act(dev(x))
-        assert_equal(host(y), host(w.w8a8_gemm_pc(xq, xs, wq_g, sw_g)), "dispatch to GEMM")
+        assert_equal(host(y), host(w.w8a8_gemm_pc(xq, xs, wq_g, sw_g)),
+                     "dispatch to quantize_act + w8a8_gemm_pc")
 
 
 @pytest.mark.parametrize("gs", [64, 128])
@@ -95,15 +98,24 @@ def test_linear_w4a8_end_to_end(torch_gpu, oracle, M, gs):
 
 
 def test_linear_workspace_checks(torch_gpu):
+    """A workspace below linear_workspace_size() is refused by the binding and,
+    called through the C ABI directly, by the library (W4A8_ERR_WORKSPACE,
+    nothing launched)."""
+    import ctypes
     import torch
     import w4a8_int8_gemm_amd as w
     x = dev(synth.activations(8, 256))
     wq = torch.zeros((16, 256), dtype=torch.int8, device="cuda")
     sw = torch.ones((16,), dtype=torch.float32, device="cuda")
+    y = torch.empty((8, 16), dtype=torch.float16, device="cuda")
     small = torch.empty((64,), dtype=torch.uint8, device="cuda")
-    with pytest.raises(w.W4A8Error) as e:
+    with pytest.raises(ValueError, match="workspace"):
         w.linear(w.Mode.W8A8_PC, x, wq, sw, workspace=small)
-    assert e.value.status == w.Status.ERR_WORKSPACE
+    P = ctypes.c_void_p
+    st = w.lib().linear(int(w.Mode.W8A8_PC), P(x.data_ptr()), 8, 256, P(wq.data_ptr()),
+                        P(sw.data_ptr()), 0, 16, P(y.data_ptr()), P(small.data_ptr()), 64,
+                        P(torch.cuda.current_stream().cuda_stream))
+    assert st == w.Status.ERR_WORKSPACE, st
 
 
 def test_int8_mv_rounds_to_nearest_even(torch_gpu, oracle):

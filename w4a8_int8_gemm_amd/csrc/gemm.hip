@@ -972,18 +972,24 @@ TileShape choose_tile(GemmMode mode, int gs, int M, int N, int K, int num_cu)
     if (M <= 64)
         return pergroup ? TileShape::T64x128 : TileShape::T64x64;
     if (!pergroup) {
-        // Large outputs: the cheapest of the three big tiles by (rounds of
-        // tiles over the compute units) x (tile area / its measured relative
-        // rate: 256x160 1, 256x128 0.9, 128x128 0.85), so that a last round
-        // left mostly empty counts against a tile shape.
+        // Large outputs: the cheapest of the big tiles by (rounds of tiles
+        // over the compute units) x (tile area / its measured relative rate:
+        // 256x320 1.08, 256x160 1, 256x128 0.9, 128x128 0.85), so that a last
+        // round left mostly empty counts against a tile shape.  The 256x320
+        // kernel needs K % 128 == 0.
         if (t128x128 >= 256) {
             const int64_t cu = num_cu > 0 ? num_cu : 1;
+            const int64_t t256x320 = (int64_t)((M + 255) / 256) * ((N + 319) / 320);
             auto rounds = [&](int64_t t) { return (double)((t + cu - 1) / cu); };
+            const double c320 = (N % 320 == 0 && K % 128 == 0)
+                                    ? rounds(t256x320) * (256.0 * 320.0 / 1.08) : 1e300;
             const double c160 = N % 160 == 0 ? rounds(t256x160) * (256.0 * 160.0) : 1e300;
             const double c256 = rounds(t256x128) * (256.0 * 128.0 / 0.9);
             const double c128 = rounds(t128x128) * (128.0 * 128.0 / 0.85);
+            if (c320 <= c160 && c320 <= c256 && c320 <= c128)
+                return TileShape::T256x320w8;
             if (c160 <= c256 && c160 <= c128)
-                return (K % 128 == 0 && N % 320 == 0) ? TileShape::T256x320w8 : TileShape::T256x160;
+                return TileShape::T256x160;
             if (c256 <= c128)
                 return TileShape::T256x128;
             return TileShape::T128x128;

@@ -1,7 +1,9 @@
 """torch-tensor wrappers over the C entry points (marshalling only).
 
-Each function checks dtype, device and contiguity, allocates missing outputs
-with torch, and calls the library on torch's current stream of the tensors'
+Each function checks every tensor's dtype, device, contiguity and exact shape
+(scales included: the C ABI receives bare pointers and cannot tell a short or
+misplaced scale vector from a valid one), allocates missing outputs with
+torch, and calls the library on torch's current stream of the tensors'
 device.  Outputs may be passed in (``out=...``) to avoid allocations.
 """
 from __future__ import annotations
@@ -13,11 +15,17 @@ import torch
 from ._lib import GemmOp, Mode, check, lib
 
 
-def _need(t, dtype, name, ndim):
+# Device type the wrappers accept (HIP devices appear as "cuda" in torch).
+_DEVICE_TYPE = "cuda"
+
+
+def _need(t, dtype, name, ndim, like=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if t.device.type != _DEVICE_TYPE:
         raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {like.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
@@ -27,13 +35,27 @@ def _need(t, dtype, name, ndim):
     return t
 
 
-def _out(t, shape, dtype, like, name):
-    if t is None:
-        return torch.empty(shape, dtype=dtype, device=like.device)
-    _need(t, dtype, name, len(shape))
+def _shaped(t, dtype, shape, name, like):
+    """t must be a contiguous `dtype` tensor of exactly `shape` on like's device."""
+    _need(t, dtype, name, len(shape), like)
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
+
+
+def _groups(K: int, group_size: int) -> int:
+    """K / group_size for a per-group operation (group size 64 or 128 dividing K)."""
+    if group_size not in (64, 128):
+        raise ValueError(f"group_size must be 64 or 128, got {group_size}")
+    if K % group_size:
+        raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
+    return K // group_size
+
+
+def _out(t, shape, dtype, like, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    return _shaped(t, dtype, shape, name, like)
 
 
 def _p(t):
@@ -88,7 +110,7 @@ def pack_weight_int4(w, group_size: int = 128, out=None, scale=None):
 
 def _gemm_shapes(xq, w, packed):
     _need(xq, torch.int8, "xq", 2)
-    _need(w, torch.uint8 if packed else torch.int8, "w", 2)
+    _need(w, torch.uint8 if packed else torch.int8, "w", 2, xq)
     M, K = xq.shape
     N = w.shape[0]
     if w.shape[1] * (2 if packed else 1) != K:
@@ -99,8 +121,8 @@ def _gemm_shapes(xq, w, packed):
 def w8a8_gemm_pc(xq, x_scale, wq, w_scale, out=None):
     """y fp16 [M, N] = (xq . wq^T) * x_scale[m] * w_scale[n]."""
     M, N, K = _gemm_shapes(xq, wq, False)
-    _need(x_scale, torch.float32, "x_scale", 1)
-    _need(w_scale, torch.float32, "w_scale", 1)
+    _shaped(x_scale, torch.float32, (M,), "x_scale", xq)
+    _shaped(w_scale, torch.float32, (N,), "w_scale", xq)
     out = _out(out, (M, N), torch.float16, xq, "out")
     with torch.cuda.device(xq.device):
         check(lib().w8a8_gemm_pc(_p(xq), _p(x_scale), _p(wq), _p(w_scale), _p(out), M, N, K,
@@ -111,8 +133,9 @@ def w8a8_gemm_pc(xq, x_scale, wq, w_scale, out=None):
 def w8a8_gemm_pg(xq, x_scale, wq, w_scale, group_size: int, out=None):
     """Per-group W8A8: x_scale [M, K/gs], w_scale [N, K/gs]."""
     M, N, K = _gemm_shapes(xq, wq, False)
-    _need(x_scale, torch.float32, "x_scale", 2)
-    _need(w_scale, torch.float32, "w_scale", 2)
+    G = _groups(K, group_size)
+    _shaped(x_scale, torch.float32, (M, G), "x_scale", xq)
+    _shaped(w_scale, torch.float32, (N, G), "w_scale", xq)
     out = _out(out, (M, N), torch.float16, xq, "out")
     with torch.cuda.device(xq.device):
         check(lib().w8a8_gemm_pg(_p(xq), _p(x_scale), _p(wq), _p(w_scale), group_size, _p(out),
@@ -123,8 +146,9 @@ def w8a8_gemm_pg(xq, x_scale, wq, w_scale, group_size: int, out=None):
 def w4a8_gemm(xq, x_scale, w4, w_scale, group_size: int, out=None):
     """W4A8: per-token x_scale [M], packed w4 [N, K/2], w_scale [N, K/gs]."""
     M, N, K = _gemm_shapes(xq, w4, True)
-    _need(x_scale, torch.float32, "x_scale", 1)
-    _need(w_scale, torch.float32, "w_scale", 2)
+    G = _groups(K, group_size)
+    _shaped(x_scale, torch.float32, (M,), "x_scale", xq)
+    _shaped(w_scale, torch.float32, (N, G), "w_scale", xq)
     out = _out(out, (M, N), torch.float16, xq, "out")
     with torch.cuda.device(xq.device):
         check(lib().w4a8_gemm(_p(xq), _p(x_scale), _p(w4), _p(w_scale), group_size, _p(out),
@@ -137,12 +161,12 @@ def int8_mv(x, wq, w_scale, out=None, return_codes: bool = False):
     if x.dim() == 2 and x.shape[0] == 1:
         x = x.reshape(-1)
     _need(x, torch.float16, "x", 1)
-    _need(wq, torch.int8, "wq", 2)
-    _need(w_scale, torch.float32, "w_scale", 1)
+    _need(wq, torch.int8, "wq", 2, x)
     K = x.shape[0]
     N = wq.shape[0]
     if wq.shape[1] != K:
         raise ValueError("wq does not match K")
+    _shaped(w_scale, torch.float32, (N,), "w_scale", x)
     out = _out(out, (N,), torch.float16, x, "out")
     xq = torch.empty((K,), dtype=torch.int8, device=x.device) if return_codes else None
     xs = torch.empty((1,), dtype=torch.float32, device=x.device) if return_codes else None
@@ -155,12 +179,12 @@ def _mv_group(fn, x, w, w_scale, group_size: int, packed: bool, out):
     if x.dim() == 2 and x.shape[0] == 1:
         x = x.reshape(-1)
     _need(x, torch.float16, "x", 1)
-    _need(w, torch.uint8 if packed else torch.int8, "w", 2)
-    _need(w_scale, torch.float32, "w_scale", 2)
+    _need(w, torch.uint8 if packed else torch.int8, "w", 2, x)
     K = x.shape[0]
     N = w.shape[0]
     if w.shape[1] * (2 if packed else 1) != K:
         raise ValueError("weight shape does not match K")
+    _shaped(w_scale, torch.float32, (N, _groups(K, group_size)), "w_scale", x)
     out = _out(out, (N,), torch.float16, x, "out")
     with torch.cuda.device(x.device):
         check(getattr(lib(), fn)(_p(x), _p(w), _p(w_scale), group_size, _p(out), N, K, _st(x)))
@@ -186,14 +210,20 @@ def linear(mode, x, w, w_scale, group_size: int = 0, workspace=None, out=None):
     mode = Mode(mode)
     _need(x, torch.float16, "x", 2)
     packed = mode == Mode.W4A8
-    _need(w, torch.uint8 if packed else torch.int8, "w", 2)
+    _need(w, torch.uint8 if packed else torch.int8, "w", 2, x)
     M, K = x.shape
     N = w.shape[0]
     if w.shape[1] * (2 if packed else 1) != K:
         raise ValueError("weight shape does not match K")
+    sw_shape = (N,) if mode == Mode.W8A8_PC else (N, _groups(K, group_size))
+    _shaped(w_scale, torch.float32, sw_shape, "w_scale", x)
     need = linear_workspace_size(mode, M, K, group_size)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    else:
+        _need(workspace, torch.uint8, "workspace", 1, x)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
     out = _out(out, (M, N), torch.float16, x, "out")
     with torch.cuda.device(x.device):
         check(lib().linear(int(mode), _p(x), M, K, _p(w), _p(w_scale), group_size, N, _p(out),
@@ -213,7 +243,7 @@ def w8a8_gemm_i32(xq, wq, out=None):
 def w8a8_gemm_pg_partials(xq, wq, group_size: int, out=None):
     """Per-group int32 partial sums [K/gs, M, N]."""
     M, N, K = _gemm_shapes(xq, wq, False)
-    out = _out(out, (K // group_size, M, N), torch.int32, xq, "out")
+    out = _out(out, (_groups(K, group_size), M, N), torch.int32, xq, "out")
     with torch.cuda.device(xq.device):
         check(lib().w8a8_gemm_pg_partials(_p(xq), _p(wq), group_size, _p(out), M, N, K, _st(xq)))
     return out
@@ -222,7 +252,7 @@ def w8a8_gemm_pg_partials(xq, wq, group_size: int, out=None):
 def w4a8_gemm_partials(xq, w4, group_size: int, out=None):
     """Per-group int32 partial sums [K/gs, M, N] against unpacked int4 codes."""
     M, N, K = _gemm_shapes(xq, w4, True)
-    out = _out(out, (K // group_size, M, N), torch.int32, xq, "out")
+    out = _out(out, (_groups(K, group_size), M, N), torch.int32, xq, "out")
     with torch.cuda.device(xq.device):
         check(lib().w4a8_gemm_partials(_p(xq), _p(w4), group_size, _p(out), M, N, K, _st(xq)))
     return out
@@ -232,12 +262,12 @@ def w8a16_gemm(x, wq, w_scale, out=None):
     """Weight-only int8 comparison GEMM: y fp16 [M, N] = w_scale[n] * (x . wq^T),
     x fp16 [M, K] (not quantized), wq int8 [N, K], w_scale fp32 [N]."""
     _need(x, torch.float16, "x", 2)
-    _need(wq, torch.int8, "wq", 2)
-    _need(w_scale, torch.float32, "w_scale", 1)
+    _need(wq, torch.int8, "wq", 2, x)
     M, K = x.shape
     N = wq.shape[0]
     if wq.shape[1] != K:
         raise ValueError(f"weight shape {tuple(wq.shape)} does not match K={K}")
+    _shaped(w_scale, torch.float32, (N,), "w_scale", x)
     out = _out(out, (M, N), torch.float16, x, "out")
     with torch.cuda.device(x.device):
         check(lib().w8a16_gemm(_p(x), _p(wq), _p(w_scale), _p(out), M, N, K, _st(x)))
@@ -249,12 +279,12 @@ def w4a16_gemm(x, w4, w_scale, group_size: int, out=None):
     fp16(code[n,k] * w_scale[n, k // gs]); x fp16 [M, K], w4 uint8 [N, K/2],
     w_scale fp32 [N, K/gs] (as from pack_weight_int4)."""
     _need(x, torch.float16, "x", 2)
-    _need(w4, torch.uint8, "w4", 2)
-    _need(w_scale, torch.float32, "w_scale", 2)
+    _need(w4, torch.uint8, "w4", 2, x)
     M, K = x.shape
     N = w4.shape[0]
     if w4.shape[1] * 2 != K:
         raise ValueError(f"weight shape {tuple(w4.shape)} does not match K={K}")
+    _shaped(w_scale, torch.float32, (N, _groups(K, group_size)), "w_scale", x)
     out = _out(out, (M, N), torch.float16, x, "out")
     with torch.cuda.device(x.device):
         check(lib().w4a16_gemm(_p(x), _p(w4), _p(w_scale), group_size, _p(out), M, N, K, _st(x)))
