@@ -195,6 +195,23 @@ w4a8_status_t linear(w4a8_mode_t mode, const w4a8_f16 *x, int64_t M, int64_t K, 
                      const float *w_scale, int32_t group_size, int64_t N, w4a8_f16 *y,
                      void *workspace, size_t workspace_bytes, w4a8_stream_t stream);
 
+/* linear() for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same argument rules, kernels and results as linear(), without a workspace
+ * argument.  The activations' int8 codes and fp32 scales are kept in a
+ * static device array of 64 MiB (2^26 bytes) that the library holds on each
+ * GPU it runs on until the process ends; its device address is looked up
+ * once per GPU.  A call whose linear_workspace_size() exceeds 64 MiB returns
+ * W4A8_ERR_WORKSPACE before anything is launched (use linear() with a
+ * workspace instead).  The call allocates nothing.  Every call on one GPU
+ * shares that GPU's array and overwrites it: calls that overlap on one GPU
+ * (different streams or threads) race, so the caller must order them, e.g.
+ * on one stream.  Nothing in the array has to start at zero -- each call
+ * writes the codes and scales it then reads. */
+w4a8_status_t linear_noalloc(w4a8_mode_t mode, const w4a8_f16 *x, int64_t M, int64_t K,
+                             const void *w, const float *w_scale, int32_t group_size, int64_t N,
+                             w4a8_f16 *y, w4a8_stream_t stream);
+
 /* --------------------------------------------------------------------------
  * Raw-accumulator exports, for checking the int32 sums bit for bit.  Same
  * main loops as the GEMMs above with the rescale replaced by a store.

@@ -14,14 +14,15 @@ library's HIP kernels; nothing here computes.
 from __future__ import annotations
 
 from ._lib import LIB_PATH, GemmOp, Mode, Status, W4A8Error, check, lib
-from .ops import (gemm_tile_config, int8_mv, is_available, linear, linear_workspace_size, pack_weight_int4,
+from .ops import (gemm_tile_config, int8_mv, is_available, linear, linear_noalloc,
+                  linear_workspace_size, pack_weight_int4,
                   quantize_act, quantize_weight_int8, w4a8_gemm, w4a8_gemm_partials,
                   w4a8_mv, w8a8_gemm_i32, w8a8_gemm_pc, w8a8_gemm_pg, w8a8_gemm_pg_partials,
                   w8a8_mv_pg, w8a16_gemm, w4a16_gemm)
 
 __all__ = [
     "LIB_PATH", "GemmOp", "Mode", "Status", "gemm_tile_config", "W4A8Error", "check", "lib", "int8_mv", "is_available",
-    "linear", "linear_workspace_size", "pack_weight_int4", "quantize_act",
+    "linear", "linear_noalloc", "linear_workspace_size", "pack_weight_int4", "quantize_act",
     "quantize_weight_int8", "w4a8_gemm", "w4a8_gemm_partials", "w8a8_gemm_i32",
     "w8a8_gemm_pc", "w8a8_gemm_pg", "w8a8_gemm_pg_partials", "w4a8_mv", "w8a8_mv_pg",
     "w8a16_gemm", "w4a16_gemm",

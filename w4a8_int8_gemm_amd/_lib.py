@@ -34,6 +34,7 @@ _SIGNATURES = {
     "w4a8_mv": [_vp, _vp, _vp, _i32, _vp, _i64, _i64, _vp],
     "linear_workspace_size": [ctypes.c_int, _i64, _i64, _i32],
     "linear": [ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _sz, _vp],
+    "linear_noalloc": [ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp],
     "w8a8_gemm_i32": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "w8a8_gemm_pg_partials": [_vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp],
     "w4a8_gemm_partials": [_vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp],

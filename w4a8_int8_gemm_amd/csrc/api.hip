@@ -188,6 +188,38 @@ w4a8_status_t check_mv_group(const char *fn, const void *x, const void *w, const
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// ---- the static scratch of linear_noalloc(): the activations' int8 codes
+// and fp32 scales live in this device array instead of a caller workspace.
+// Each device the library runs on holds its own copy (placed when the code
+// object is loaded there) until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it only names the symbol): the
+// device address is looked up per device with hipGetSymbolAddress and kept.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<uintptr_t> g_scratch_dev[64];     // per device ordinal; 0 = not looked up yet
+
+// Device address of the current device's copy of `scratch`.
+w4a8_status_t scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64)
+        return fail(W4A8_ERR_DEVICE, "no HIP device for the static scratch (%s)",
+                    hipGetErrorString(e));
+    uintptr_t p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (p == 0) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(W4A8_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d failed: %s",
+                        dev, hipGetErrorString(e));
+        p = reinterpret_cast<uintptr_t>(ptr);
+        g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+    *out = reinterpret_cast<void *>(p);
+    return W4A8_OK;
+}
+
 GemmArgs make_args(const int8_t *xq, const float *sa, const void *w, const float *sw, void *out,
                    int64_t M, int64_t N, int64_t K, int gs)
 {
@@ -256,6 +288,77 @@ w4a8_status_t run_quant(const char *fn, const uint16_t *x, int64_t rows, int64_t
         return st;
     launch_quantize_rows(x, rows, (int)K, gs, qmax, q, scale, int4, (hipStream_t)stream);
     return check_launch(fn);
+}
+
+}  // namespace
+
+namespace {
+
+// linear()'s argument rules (no HIP calls): the mode, then the GEMM's rules,
+// whatever M is.  Sets *empty for a call with nothing to do.
+w4a8_status_t check_linear(const char *fn, w4a8_mode_t mode, const w4a8_f16 *x, int64_t M,
+                           int64_t K, const void *w, const float *w_scale, int32_t group_size,
+                           int64_t N, w4a8_f16 *y, bool *empty)
+{
+    *empty = false;
+    if (mode != W4A8_MODE_W8A8_PC && mode != W4A8_MODE_W8A8_PG && mode != W4A8_MODE_W4A8)
+        return fail(W4A8_ERR_INVALID_ARG, "%s: unknown mode %d", fn, (int)mode);
+    const bool pg = mode != W4A8_MODE_W8A8_PC;
+    const int32_t gs = pg ? group_size : 0;
+    w4a8_status_t st = check_gemm(fn, x, w, y, w_scale, w_scale, M, N, K, gs, pg, true);
+    if (st != W4A8_OK)
+        return st;
+    if (M == 0 || N == 0) {
+        *empty = true;
+        return W4A8_OK;
+    }
+    if (!x || !aligned16(x))
+        return fail(x ? W4A8_ERR_ALIGNMENT : W4A8_ERR_INVALID_ARG, "%s: bad x", fn);
+    return W4A8_OK;
+}
+
+// The layer on checked arguments (check_linear) with the given workspace,
+// which may be the static scratch (linear_noalloc).
+w4a8_status_t linear_run(const char *fn, w4a8_mode_t mode, const w4a8_f16 *x, int64_t M,
+                         int64_t K, const void *w, const float *w_scale, int32_t group_size,
+                         int64_t N, w4a8_f16 *y, void *workspace, size_t workspace_bytes,
+                         w4a8_stream_t stream)
+{
+    const int32_t act_gs = (mode == W4A8_MODE_W8A8_PG) ? group_size : 0;
+    w4a8_status_t st;
+    if (M == 1 && K <= kMaxKMv) {                 // decode: the matrix-vector kernels
+        switch (mode) {
+        case W4A8_MODE_W8A8_PC:
+            return int8_mv(x, static_cast<const int8_t *>(w), w_scale, y, N, K, nullptr, nullptr,
+                           stream);
+        case W4A8_MODE_W8A8_PG:
+            return w8a8_mv_pg(x, static_cast<const int8_t *>(w), w_scale, group_size, y, N, K,
+                              stream);
+        default:
+            return w4a8_mv(x, static_cast<const uint8_t *>(w), w_scale, group_size, y, N, K,
+                           stream);
+        }
+    }
+    const size_t need = linear_workspace_size(mode, M, K, group_size);
+    if (!workspace || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(W4A8_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) needed, "
+                    "got %zu", fn, need, workspace_bytes);
+    int8_t *xq = static_cast<int8_t *>(workspace);
+    float *xs = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)M * K));
+    st = quantize_act(x, M, K, act_gs, xq, xs, stream);
+    if (st != W4A8_OK)
+        return st;
+    switch (mode) {
+    case W4A8_MODE_W8A8_PC:
+        return run_pc(fn, xq, xs, static_cast<const int8_t *>(w), w_scale, y, M, N, K, stream);
+    case W4A8_MODE_W8A8_PG:
+        return run_gemm(fn, GemmMode::PG,
+                        make_args(xq, xs, w, w_scale, y, M, N, K, group_size), stream);
+    default:
+        return run_w4(fn, xq, xs, static_cast<const uint8_t *>(w), w_scale, group_size, y, M,
+                      N, K, stream);
+    }
 }
 
 }  // namespace
@@ -416,52 +519,38 @@ w4a8_status_t linear(w4a8_mode_t mode, const w4a8_f16 *x, int64_t M, int64_t K, 
                      const float *w_scale, int32_t group_size, int64_t N, w4a8_f16 *y,
                      void *workspace, size_t workspace_bytes, w4a8_stream_t stream)
 {
-    if (mode != W4A8_MODE_W8A8_PC && mode != W4A8_MODE_W8A8_PG && mode != W4A8_MODE_W4A8)
-        return fail(W4A8_ERR_INVALID_ARG, "linear: unknown mode %d", (int)mode);
-    const bool pg = mode != W4A8_MODE_W8A8_PC;
-    const int32_t gs = pg ? group_size : 0;
-    const int32_t act_gs = (mode == W4A8_MODE_W8A8_PG) ? group_size : 0;
-    // the GEMM's rules decide what linear accepts, whatever M is
-    w4a8_status_t st = check_gemm("linear", x, w, y, w_scale, w_scale, M, N, K, gs, pg, true);
-    if (st != W4A8_OK)
-        return st;
-    if (M == 0 || N == 0)
-        return ok();
-    if (!x || !aligned16(x))
-        return fail(x ? W4A8_ERR_ALIGNMENT : W4A8_ERR_INVALID_ARG, "linear: bad x");
-    if (M == 1 && K <= kMaxKMv) {                 // decode: the matrix-vector kernels
-        switch (mode) {
-        case W4A8_MODE_W8A8_PC:
-            return int8_mv(x, static_cast<const int8_t *>(w), w_scale, y, N, K, nullptr, nullptr,
-                           stream);
-        case W4A8_MODE_W8A8_PG:
-            return w8a8_mv_pg(x, static_cast<const int8_t *>(w), w_scale, group_size, y, N, K,
-                              stream);
-        default:
-            return w4a8_mv(x, static_cast<const uint8_t *>(w), w_scale, group_size, y, N, K,
-                           stream);
-        }
-    }
+    bool empty;
+    w4a8_status_t st = check_linear("linear", mode, x, M, K, w, w_scale, group_size, N, y, &empty);
+    if (st != W4A8_OK || empty)
+        return st == W4A8_OK ? ok() : st;
+    return linear_run("linear", mode, x, M, K, w, w_scale, group_size, N, y, workspace,
+                      workspace_bytes, stream);
+}
+
+w4a8_status_t linear_noalloc(w4a8_mode_t mode, const w4a8_f16 *x, int64_t M, int64_t K,
+                             const void *w, const float *w_scale, int32_t group_size, int64_t N,
+                             w4a8_f16 *y, w4a8_stream_t stream)
+{
+    const char *fn = "linear_noalloc";
+    bool empty;
+    w4a8_status_t st = check_linear(fn, mode, x, M, K, w, w_scale, group_size, N, y, &empty);
+    if (st != W4A8_OK || empty)
+        return st == W4A8_OK ? ok() : st;
     const size_t need = linear_workspace_size(mode, M, K, group_size);
-    if (!workspace || workspace_bytes < need ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return fail(W4A8_ERR_WORKSPACE, "linear: workspace of %zu bytes (256-byte aligned) needed, "
-                    "got %zu", need, workspace_bytes);
-    int8_t *xq = static_cast<int8_t *>(workspace);
-    float *xs = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)M * K));
-    st = quantize_act(x, M, K, act_gs, xq, xs, stream);
-    if (st != W4A8_OK)
-        return st;
-    switch (mode) {
-    case W4A8_MODE_W8A8_PC:
-        return run_pc("linear", xq, xs, static_cast<const int8_t *>(w), w_scale, y, M, N, K, stream);
-    case W4A8_MODE_W8A8_PG:
-        return run_gemm("linear", GemmMode::PG,
-                        make_args(xq, xs, w, w_scale, y, M, N, K, group_size), stream);
-    default:
-        return run_w4("linear", xq, xs, static_cast<const uint8_t *>(w), w_scale, group_size, y, M,
-                      N, K, stream);
+    if (need > kScratchBytes)
+        return fail(W4A8_ERR_WORKSPACE, "%s: M=%lld, K=%lld need %zu bytes of scratch; the "
+                    "static array holds %zu (call linear() with a workspace)", fn, (long long)M,
+                    (long long)K, need, kScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        st = check_device();
+        if (st != W4A8_OK)
+            return st;
+        st = scratch_address(&ws);
+        if (st != W4A8_OK)
+            return st;
     }
+    return linear_run(fn, mode, x, M, K, w, w_scale, group_size, N, y, ws, kScratchBytes, stream);
 }
 
 w4a8_status_t w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int32_t *c, int64_t M, int64_t N,

@@ -231,6 +231,27 @@ def linear(mode, x, w, w_scale, group_size: int = 0, workspace=None, out=None):
     return out
 
 
+def linear_noalloc(mode, x, w, w_scale, group_size: int = 0, out=None):
+    """linear() without a workspace: the library keeps the activation codes in
+    a static 64 MiB device array (no allocation in the call; calls that overlap
+    on one GPU race).  Pass ``out`` to keep this wrapper allocation-free too."""
+    mode = Mode(mode)
+    _need(x, torch.float16, "x", 2)
+    packed = mode == Mode.W4A8
+    _need(w, torch.uint8 if packed else torch.int8, "w", 2, x)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] * (2 if packed else 1) != K:
+        raise ValueError("weight shape does not match K")
+    sw_shape = (N,) if mode == Mode.W8A8_PC else (N, _groups(K, group_size))
+    _shaped(w_scale, torch.float32, sw_shape, "w_scale", x)
+    out = _out(out, (M, N), torch.float16, x, "out")
+    with torch.cuda.device(x.device):
+        check(lib().linear_noalloc(int(mode), _p(x), M, K, _p(w), _p(w_scale), group_size, N,
+                                   _p(out), _st(x)))
+    return out
+
+
 def w8a8_gemm_i32(xq, wq, out=None):
     """Raw int32 sums [M, N] of the per-channel GEMM's main loop."""
     M, N, K = _gemm_shapes(xq, wq, False)
