@@ -40,7 +40,9 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
 # machine: context only.
 PAGES_TOPS_M5PRO = 2 * 4096 * 10240 * 2560 / 4.41e-3 / 1e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_pc_headline_traffic.json")
-GEMM_SOURCE = os.path.join(ROOT, "w4a8_int8_gemm_amd", "csrc", "gemm.hip")
+# the dominant kernel's sources: the counters go stale when either changes
+GEMM_SOURCES = [os.path.join(ROOT, "w4a8_int8_gemm_amd", "csrc", f)
+                for f in ("gemm_pc.hip", "lds_copy.hpp")]
 
 
 def log(*a):
@@ -68,8 +70,11 @@ def parse():
 
 
 def gemm_source_hash() -> str:
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(per_launch_bytes_alg: float):
