@@ -35,6 +35,14 @@ if ROOT not in sys.path:
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA (published), in tera-ops/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
+# Vector ALU: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz (the clock the MFMA
+# figure assumes), in lane-operations per second.
+PEAK_VALU_OPS = 256 * 4 * 16 * 2.4e9
+# VALU operations per output element per K group of the per-group fold:
+# convert the int32 partial, form the token-by-channel scale, fused
+# multiply-add (per-group W8A8); convert and fused multiply-add (W4A8, whose
+# token scale is applied once at the end).
+FOLD_VALU_OPS = {"pg": 3, "w4a8": 2}
 # The pages' figure for this exact workload (per-channel W8A8, N=10240, K=2560,
 # M=4096): 4.41 ms on Apple M5 Pro, i.e. 2*M*N*K / 4.41 ms = 48.7 TOPS.  Another
 # machine: context only.
@@ -77,17 +85,18 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(per_launch_bytes_alg: float):
-    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or None
-    if there are none or the kernel source changed since they were taken."""
+def counters_from_profiles():
+    """The GEMM's committed rocprofv3 counter figures (HBM bytes per launch,
+    shader clock and MFMA-busy fraction of a counter run), or {} if there are
+    none or the kernel's sources changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     if t.get("gemm_source_sha256_16") != gemm_source_hash():
-        return None
-    return t.get("bytes_per_launch")
+        return {}
+    return t
 
 
 def kernel_sample():
@@ -212,7 +221,95 @@ def copy_probe():
     log(f"copy probe: 5 copies of {n} bytes")
 
 
-def suite(reps):
+def copy_rate_gbs(reps=20):
+    """Measured device copy rate (bytes read + written per second) of a plain
+    512 MiB device-to-device copy, timed after 25 ms of copies: the practical
+    ceiling of an HBM-bound kernel on this GPU."""
+    import torch
+    n = 512 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    t_s = time.perf_counter()
+    while time.perf_counter() - t_s < 0.025:
+        b.copy_(a)
+        torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2.0 * n / us / 1e3
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_timings(target_s=1.0):
+    """The oracle (as it stands, untuned) on every workload shape: quantize,
+    int32 GEMM and fp64 epilogue on the first rows of the shape's activations
+    (rows doubled until one run takes target_s, or all rows), on one core and
+    on all the cores the oracle uses by default; the weights are quantized
+    beforehand (offline, untimed).  Prints one line per shape."""
+    import numpy as np
+    import oracle
+    import synth
+
+    cores = oracle.num_threads()
+    print(f"oracle timings: CPU {cpu_model()}, {os.cpu_count()} logical CPUs visible, "
+          f"oracle threads 1 and {cores}", flush=True)
+
+    def rate(mode, x, wq, sw, gs, N, K):
+        rows, dt = 1, 0.0
+        while True:
+            t0 = time.perf_counter()
+            oracle.linear(mode, x[:rows], wq, sw, gs)
+            dt = time.perf_counter() - t0
+            if dt >= target_s or rows >= x.shape[0]:
+                return rows, dt
+            rows = min(x.shape[0], rows * 2 if dt < target_s / 8 else
+                       max(rows + 1, int(rows * target_s / max(dt, 1e-6))))
+
+    lines = []
+    try:
+        for name, wl in synth.WORKLOADS.items():
+            mode, gs = wl["mode"], wl["gs"]
+            for (M, N, K) in wl["shapes"]:
+                x = synth.activations(M, K, seed=1, outliers=wl["outliers"])
+                wt = synth.weights(N, K, seed=2)
+                if mode == "w4a8":
+                    wq, sw = oracle.pack_weight_int4(wt, gs)
+                else:
+                    wq, sw = oracle.quantize_weight_int8(wt, gs if mode == "pg" else 0)
+                del wt
+                res = []
+                for th in (1, cores):
+                    oracle.set_num_threads(th)
+                    rows, dt = rate(mode, x, wq, sw, gs, N, K)
+                    gops = 2.0 * rows * N * K / dt / 1e9
+                    res.append(f"{th:3d} core{'s' if th > 1 else ' '} {gops:8.2f} GOPS "
+                               f"({rows:5d} rows in {dt:5.2f} s; whole shape "
+                               f"{2.0 * M * N * K / gops / 1e9:8.1f} s)")
+                lines.append(f"oracle {name:10s} M={M:5d} N={N:5d} K={K:5d}  " + " | ".join(res))
+                print(lines[-1], flush=True)
+    finally:
+        oracle.set_num_threads(cores)
+    return lines
+
+
+def suite(reps, with_oracle=True):
     """Per-workload kernel timings (not the JSON line): every shape of
     synth.WORKLOADS through its path, each kernel `reps` times back to back
     between two events, through the C entry points.  The decode shapes (M=1),
@@ -235,6 +332,10 @@ def suite(reps):
 
     def ptr(t):
         return P(t.data_ptr())
+
+    copy_gbs = copy_rate_gbs()
+    print(f"device copy rate (512 MiB copy, read + write): {copy_gbs:.0f} GB/s "
+          f"({100 * copy_gbs / PEAK_HBM_GBS:.0f}% of HBM peak)", flush=True)
 
     def b2b(fn):
         fn()
@@ -283,7 +384,8 @@ def suite(reps):
                 del flush
                 wbytes = N * K + 2 * K + 6 * N
                 rows.append(f"{name:10s} M={M:5d} N={N:5d} K={K:5d}  int8_mv {us:8.2f} us warm  "
-                            f"{wbytes / us / 1e3:7.0f} GB/s ({100 * wbytes / us / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak)")
+                            f"{wbytes / us / 1e3:7.0f} GB/s ({100 * wbytes / us / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak, "
+                            f"{100 * wbytes / us / 1e3 / copy_gbs:.0f}% of the copy rate)")
                 continue
             q = lambda: w.check(L.quantize_act(ptr(x), M, K, act_gs, ptr(xq), ptr(xs), sp))
             if mode == "pc":
@@ -308,10 +410,19 @@ def suite(reps):
                 torch.cuda.synchronize()
                 del flush
             qbytes = 3 * M * K
+            bound = ""
+            if mode in FOLD_VALU_OPS:
+                # the kernel's floor: the larger of its MFMA time and its fold's
+                # VALU time, both at the published rates
+                mfma_us = ops / (PEAK_INT8_TOPS * 1e6)
+                valu_us = M * N * (K // gs) * FOLD_VALU_OPS[mode] / PEAK_VALU_OPS * 1e6
+                bound = (f" | bound max(MFMA {mfma_us:.1f}, VALU fold {valu_us:.1f}) us: "
+                         f"{100 * max(mfma_us, valu_us) / gus:4.1f}% of it")
             rows.append(f"{name:10s} M={M:5d} N={N:5d} K={K:5d}  quantize {qus:7.2f} us "
-                        f"({qbytes / qus / 1e3:5.0f} GB/s) | gemm {gus:8.2f} us "
+                        f"({qbytes / qus / 1e3:5.0f} GB/s, {100 * qbytes / qus / 1e3 / copy_gbs:3.0f}% of copy rate)"
+                        f" | gemm {gus:8.2f} us "
                         f"{ops / gus / 1e6:7.1f} TOPS ({100 * ops / gus / 1e6 / PEAK_INT8_TOPS:4.1f}% "
-                        f"of int8 peak) | step {ops / (qus + gus) / 1e6:7.1f} TOPS")
+                        f"of int8 peak){bound} | step {ops / (qus + gus) / 1e6:7.1f} TOPS")
             print(rows[-1], flush=True)
             del x, y, wq, sw, xq, xs
             torch.cuda.empty_cache()
@@ -353,7 +464,8 @@ def suite(reps):
         kern = "w4a8_mv" if mode == "w4a8" else "w8a8_mv_pg"
         rows.append(f"{mode + '_mv':10s} M=    1 N={N:5d} K={K:5d}  {kern} gs={gs} {us:8.2f} us warm  "
                     f"{wbytes / us / 1e3:7.0f} GB/s ({100 * wbytes / us / 1e3 / PEAK_HBM_GBS:.0f}% "
-                    f"of HBM peak) | quantize + GEMM at M=1 {path_us:8.2f} us")
+                    f"of HBM peak, {100 * wbytes / us / 1e3 / copy_gbs:.0f}% of the copy rate) | "
+                    f"quantize + GEMM at M=1 {path_us:8.2f} us")
         print(rows[-1], flush=True)
         del x, y, wq, sw, xq, xs
         torch.cuda.empty_cache()
@@ -388,13 +500,15 @@ def suite(reps):
         del x, y, xq, xs
     del wq, sw, w4, s4
     torch.cuda.empty_cache()
+    if with_oracle:
+        rows += oracle_timings()
     print("\n".join(rows), flush=True)
 
 
 def cpu_baseline(x, wt_q, sw, M, N, K, target_s):
-    """The oracle (untuned) on the first `rows` tokens of the same workload."""
+    """The oracle (untuned) on the first `rows` tokens of the same workload,
+    with all the threads it uses by default, then on one core."""
     import oracle
-    import numpy as np
 
     def run(rows):
         t0 = time.perf_counter()
@@ -403,19 +517,31 @@ def cpu_baseline(x, wt_q, sw, M, N, K, target_s):
         assert r["y"].shape == (rows, N)
         return dt
 
-    rows = 8
-    dt = run(rows)
-    while dt < 0.5 and rows < M:
-        rows = min(M, rows * 4)
+    def sample(target):
+        rows = 8
         dt = run(rows)
-    if dt < target_s and rows < M:
-        rows = int(min(M, max(rows, rows * target_s / max(dt, 1e-6))))
-        dt = run(rows)
+        while dt < 0.5 and rows < M:
+            rows = min(M, rows * 4)
+            dt = run(rows)
+        if dt < target and rows < M:
+            rows = int(min(M, max(rows, rows * target / max(dt, 1e-6))))
+            dt = run(rows)
+        return rows, dt
+
+    cores = oracle.num_threads()
+    rows, dt = sample(target_s)
     tops = 2.0 * rows * N * K / dt / 1e12
-    return {"value": round(tops, 6), "unit": "TOPS", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 3),
+    try:
+        oracle.set_num_threads(1)
+        rows1, dt1 = sample(target_s / 3)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(tops, 6), "unit": "TOPS", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3), "cpu": cpu_model(),
             "sample": f"first {rows} of {M} tokens (all N={N}, K={K}): quantize, int32 GEMM, "
-                      f"fp64 rescale, same inputs as the GPU run"}
+                      f"fp64 rescale, same inputs as the GPU run",
+            "one_core": {"value": round(2.0 * rows1 * N * K / dt1 / 1e12, 6), "unit": "TOPS",
+                         "seconds": round(dt1, 3), "sample": f"first {rows1} of {M} tokens"}}
 
 
 def main():
@@ -440,7 +566,7 @@ def main():
         kernel_sample()
         return
     if args.suite:
-        suite(args.steps)
+        suite(args.steps, with_oracle=not args.no_cpu_baseline)
         return
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -552,7 +678,10 @@ def main():
     quant_ms = quant_us * 1e-3
     quant_bytes = M * K * 2 + M * K + M * 4            # read fp16 x, write int8 codes + scales
     gemm_bytes_alg = M * K + N * K + M * N * 2 + (M + N) * 4
-    traffic = traffic_from_profiles(gemm_bytes_alg)
+    counters = counters_from_profiles()
+    traffic = counters.get("bytes_per_launch")
+    clk = counters.get("shader_clock_ghz")
+    copy_gbs = copy_rate_gbs()
 
     out = {
         "metric": "W8A8 prefill TOPS incl. act-quant, N=10240 K=2560 M=4096; % int8 MFMA peak",
@@ -579,11 +708,20 @@ def main():
                      "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
                      "avg_launch_us": round(gemm_ms * 1e3, 2),
-                     "algorithmic_bytes": gemm_bytes_alg},
+                     "algorithmic_bytes": gemm_bytes_alg,
+                     # the peak scaled to the shader clock a counter run of this
+                     # kernel measured (power-limited below the 2.4 GHz the
+                     # published figure assumes)
+                     "sustained_clock_ghz": clk,
+                     "frac_at_sustained_clock": (round(gemm_tops / (PEAK_INT8_TOPS * clk / 2.4), 4)
+                                                 if clk else None),
+                     "mfma_busy_counters": counters.get("mfma_busy")},
         "quantize_act": {"avg_launch_us": round(quant_ms * 1e3, 2),
                          "achieved_GBps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
                          "peak_GBps": PEAK_HBM_GBS,
-                         "frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                         "frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "copy_GBps": round(copy_gbs, 1),
+                         "frac_of_copy": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / copy_gbs, 4)},
         "gpu_us_per_step": round(gpu_step_us, 2),
         "linear_ms_per_step": round(linear_ms, 5),
         "linear_matches_kernels": same,
