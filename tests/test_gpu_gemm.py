@@ -3,10 +3,12 @@ bit, fp16 outputs within tolerance, against the oracle on the same seeded
 int8 codes and scales (drawn by the input generator, not by either side).
 
 Shapes are chosen to exercise every tile configuration the library selects
-(32x32, 64x64, 64x128, 128x128, 256x128, 256x160, 256x320), ragged M/N edges,
-N not a multiple of 4 (scalar stores), and K with a half-filled last stage
-(K % 128 == 64); test_tile_selection asserts which configuration the large
-shapes run (gemm_tile_config)."""
+(32x32, 64x64, 64x128, 128x128, 256x128, 256x160, 256x320, and the few-token
+row-range form with each of its token paddings 16/32/64/128, one or several
+passes over a workgroup's rows, and workgroups with no K to do), ragged M/N
+edges, N not a multiple of 4 (scalar stores), and K with a half-filled last
+stage (K % 128 == 64); test_tile_selection asserts which configuration the
+shapes the tests rely on run (gemm_tile_config)."""
 import numpy as np
 import pytest
 
@@ -46,6 +48,15 @@ PC_SHAPES = [
     # tiles (the four-stage ring across tile boundaries), with stages per
     # tile below and above the ring depth
     (8, 49160, 256), (8, 49152, 640), (40, 40968, 192),
+    # the few-token row-range form: tokens padded to 16, 32, 64, 128; rows per
+    # workgroup 8 (N=2048) to 40 (N=10240); N ragged against the 8-row units
+    # and not a multiple of 4; a K tail; K = 64 (one 64-byte stage: three of
+    # the four waves have none); K / 64 odd; N < 8; several passes per
+    # workgroup (more rows than one pass holds: N=40000 at 24 tokens, and
+    # N=49160 at 8 tokens below)
+    (5, 10240, 2560), (17, 4099, 448), (33, 2048, 1024), (100, 8192, 2560),
+    (128, 4096, 4096), (65, 6150, 320), (7, 5, 64), (128, 1030, 64), (20, 8190, 4160),
+    (24, 40000, 192),
     # 1-4 tokens: the matrix-vector form, one shape per lane split (K / 16
     # chunks <= 64, 128, 160, 256, more), N ragged against its 16 or 4 rows
     # per workgroup; M * K at 65536 (last one on this path) and just above
@@ -72,6 +83,15 @@ EXPECTED_TILES = {
     (1500, 10240, 192): (256, 128, 4),     # K % 128 != 0; 2 rounds of 256x128 beat 256x160
     (2000, 8200, 1024): (128, 128, 4),     # N % 160 != 0
     (2048, 10240, 128): (256, 320, 8),     # one K-stage per tile
+    # few tokens: the row-range form (tokens padded to 16, rows of one pass)
+    (5, 10240, 2560): (16, 48, 4),         # 40 rows per workgroup
+    (32, 10240, 2560): (32, 48, 4),
+    (8, 49160, 256): (16, 128, 4),         # 192 rows per workgroup: two passes
+    (100, 8192, 2560): (128, 32, 4),       # 32 rows per workgroup
+    (128, 4096, 4096): (128, 16, 4),
+    (7, 5, 64): (16, 16, 4),
+    (24, 40000, 192): (32, 128, 4),        # 160 rows per workgroup: two passes
+    (64, 10240, 2560): (64, 64, 2),        # 33-128 tokens with N > 8192: tiles
 }
 
 

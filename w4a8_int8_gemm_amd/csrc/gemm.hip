@@ -872,6 +872,7 @@ template <GemmMode MODE, int GS> constexpr bool tile_ok(TileShape t)
     case TileShape::T256x128w8: return T::pergroup && !pg64;
     case TileShape::T256x160: return !T::pergroup;
     case TileShape::T256x320w8: return false;       // a kernel of its own
+    case TileShape::TSkinny: return false;          // a kernel of its own
     }
     return false;
 }
@@ -896,6 +897,7 @@ int with_tile(TileShape t, A &&...args)
         W4A8_TILE(T256x128w8, 256, 128, 4, 2)
         W4A8_TILE(T256x160, 256, 160, 4, 1)
     case TileShape::T256x320w8:
+    case TileShape::TSkinny:
         return -1;
     }
 #undef W4A8_TILE
@@ -919,6 +921,8 @@ void launch_mode(const GemmArgs &a, hipStream_t st)
     const TileShape t = choose_tile(MODE, GS, a.M, a.N, a.K, a.num_cu);
     if (t == TileShape::T256x320w8)
         launch_gemm_pc2(MODE == GemmMode::I32, a, st, true);
+    else if (t == TileShape::TSkinny)
+        launch_gemm_skinny(MODE == GemmMode::I32, a, st, true);
     else
         with_tile<MODE, GS, LaunchCfgF>(t, a, st);
 }
@@ -936,6 +940,8 @@ TileInfo info_mode(const GemmArgs &a)
     const TileShape t = choose_tile(MODE, GS, a.M, a.N, a.K, a.num_cu);
     if (t == TileShape::T256x320w8)
         return launch_gemm_pc2(MODE == GemmMode::I32, a, nullptr, false);
+    if (t == TileShape::TSkinny)
+        return launch_gemm_skinny(MODE == GemmMode::I32, a, nullptr, false);
     TileInfo r = tile_dims(t);
     const int64_t tiles = (int64_t)((a.M + r.bm - 1) / r.bm) * ((a.N + r.bn - 1) / r.bn);
     r.per_cu = resident_groups<MODE, GS>(t);
@@ -962,6 +968,13 @@ TileShape choose_tile(GemmMode mode, int gs, int M, int N, int K, int num_cu)
     const int64_t t256x160 = (int64_t)((M + 255) / 256) * ((N + 159) / 160);
     const int64_t t256x128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
     const int64_t t128x128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    // Few tokens per channel: the product is bound by one pass over the
+    // weights, and the row-range form (each compute unit streams a range of
+    // weight rows against all tokens) measured faster up to 32 tokens, and up
+    // to 128 where the output is too narrow (N <= 8192) for enough tiles.
+    // Every compute unit reads all of X, so beyond that the tiles win.
+    if (!pergroup && (M <= 32 || (M <= 128 && N <= 8192)))
+        return TileShape::TSkinny;
     // Few tokens: the weights are streamed once and the output is small, so
     // the tile count decides how many compute units pull weights.  32x32
     // single-wave tiles (int8 weights) and 64x64 ones (per-channel) give four
@@ -1021,6 +1034,7 @@ TileInfo tile_dims(TileShape t)
     case TileShape::T256x128w8: r.bm = 256; r.bn = 128; r.waves = 8; break;
     case TileShape::T256x160: r.bm = 256; r.bn = 160; r.waves = 4; break;
     case TileShape::T256x320w8: r.bm = 256; r.bn = 320; r.waves = 8; break;
+    case TileShape::TSkinny: r.bm = 0; r.bn = 0; r.waves = 4; break;   // depends on M and N
     }
     return r;
 }

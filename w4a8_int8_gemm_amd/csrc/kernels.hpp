@@ -41,7 +41,8 @@ void launch_gemm(GemmMode mode, const GemmArgs &a, hipStream_t st);
 // waves, i.e. two per SIMD, where the default is four).
 enum class TileShape : int {
     T32x32, T32x128, T64x64, T64x128, T128x128, T128x128w8, T256x128, T256x128w8, T256x160,
-    T256x320w8   // the per-channel kernel of its own (K % 128 == 0)
+    T256x320w8,  // the per-channel kernel of its own (K % 128 == 0)
+    TSkinny      // per-channel, few tokens: weight rows per workgroup, K split over its waves
 };
 struct TileInfo {
     int bm, bn, waves;    // output tile per workgroup and its wavefronts
@@ -60,6 +61,11 @@ TileInfo gemm_info(GemmMode mode, const GemmArgs &a);
 // waves (K % 128 == 0); launches only when `launch`, and returns its tile and
 // grid either way.
 TileInfo launch_gemm_pc2(bool i32_out, const GemmArgs &a, hipStream_t st, bool launch);
+
+// The per-channel (or raw int32) GEMM for few tokens (M <= 128, K % 64 == 0):
+// each workgroup streams a contiguous range of weight rows against all tokens.
+// Its TileInfo gives bm = the tokens padded to 16, bn = the rows of one pass.
+TileInfo launch_gemm_skinny(bool i32_out, const GemmArgs &a, hipStream_t st, bool launch);
 
 // Few-token per-channel product (1 <= M <= 4, M * K <= 64 KiB): the weight
 // rows streamed whole against the tokens' codes in LDS; equals the
