@@ -99,6 +99,10 @@ WORKLOADS = {
     "w4a8_layer": dict(mode="w4a8", shapes=[(4516, 6144, 4096), (4516, 4096, 4096),
                                             (4516, 24576, 4096), (4516, 4096, 12288)],
                        gs=128, outliers=False),
+    # one GPU's share when a layer's output columns are split over eight GPUs:
+    # the headline layer (N = 10240 / 8) and the W4A8 gate_up linear (24576 / 8)
+    "pc_shard8": dict(mode="pc", shapes=[(4096, 1280, 2560)], gs=0, outliers=True),
+    "w4a8_shard8": dict(mode="w4a8", shapes=[(4516, 3072, 4096)], gs=128, outliers=False),
 }
 
 # The headline shape: per-channel W8A8 prefill at M=4096, N=10240, K=2560.

@@ -3,7 +3,7 @@ bit, fp16 outputs within tolerance, against the oracle on the same seeded
 int8 codes and scales (drawn by the input generator, not by either side).
 
 Shapes are chosen to exercise every tile configuration the library selects
-(32x32, 64x64, 64x128, 128x128, 256x128, 256x160, 256x320, and the few-token
+(32x32, 64x64, 64x128, 128x128, 128x160, 256x128, 256x160, 256x320, and the few-token
 row-range form with each of its token paddings 16/32/64/128, one or several
 passes over a workgroup's rows, and workgroups with no K to do), ragged M/N
 edges, N not a multiple of 4 (scalar stores), and K with a half-filled last
@@ -39,6 +39,9 @@ PC_SHAPES = [
     # ring of two wraps four times per tile and the stage stream crosses
     # tile boundaries); then a ragged last tile row (4000 = 15 * 256 + 160)
     (4096, 10240, 1024), (4000, 10240, 640),
+    # 128x160 tiles (one round where 256-row tiles leave compute units idle):
+    # ragged M, a K tail
+    (4000, 1280, 640), (3900, 1280, 704),
     # few tokens: 32x32 and 64x64 tiles, N ragged against them (scalar stores
     # where N % 8 != 0), a K tail; the M = 32 / 64 rows of the N=10240 K=2560
     # layer
@@ -83,6 +86,8 @@ EXPECTED_TILES = {
     (1500, 10240, 192): (256, 128, 4),     # K % 128 != 0; 2 rounds of 256x128 beat 256x160
     (2000, 8200, 1024): (128, 128, 4),     # N % 160 != 0
     (2048, 10240, 128): (256, 320, 8),     # one K-stage per tile
+    (4096, 1280, 2560): (128, 160, 4),     # 256 tiles of 128x160: one round
+    (4000, 1280, 640): (128, 160, 4),
     # few tokens: the row-range form (tokens padded to 16, rows of one pass)
     (5, 10240, 2560): (16, 48, 4),         # 40 rows per workgroup
     (32, 10240, 2560): (32, 48, 4),

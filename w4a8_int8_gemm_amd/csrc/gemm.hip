@@ -871,6 +871,7 @@ template <GemmMode MODE, int GS> constexpr bool tile_ok(TileShape t)
     case TileShape::T256x128: return !T::pergroup;
     case TileShape::T256x128w8: return T::pergroup && !pg64;
     case TileShape::T256x160: return !T::pergroup;
+    case TileShape::T128x160: return !T::pergroup;
     case TileShape::T256x320w8: return false;       // a kernel of its own
     case TileShape::TSkinny: return false;          // a kernel of its own
     }
@@ -896,6 +897,7 @@ int with_tile(TileShape t, A &&...args)
         W4A8_TILE(T256x128, 256, 128, 2, 2)
         W4A8_TILE(T256x128w8, 256, 128, 4, 2)
         W4A8_TILE(T256x160, 256, 160, 4, 1)
+        W4A8_TILE(T128x160, 128, 160, 4, 1)
     case TileShape::T256x320w8:
     case TileShape::TSkinny:
         return -1;
@@ -987,9 +989,11 @@ TileShape choose_tile(GemmMode mode, int gs, int M, int N, int K, int num_cu)
     if (!pergroup) {
         // Large outputs: the cheapest of the big tiles by (rounds of tiles
         // over the compute units) x (tile area / its measured relative rate:
-        // 256x320 1.08, 256x160 1, 256x128 0.9, 128x128 0.85), so that a last
-        // round left mostly empty counts against a tile shape.  The 256x320
-        // kernel needs K % 128 == 0.
+        // 256x320 1.08, 256x160 1, 256x128 0.9, 128x128 0.85, 128x160 0.8),
+        // so that a last round left mostly empty counts against a tile shape
+        // (128x160 fills the compute units where the 256-row tiles leave
+        // many idle, e.g. 4096 x 1280).  The 256x320 kernel needs
+        // K % 128 == 0.
         if (t128x128 >= 256) {
             const int64_t cu = num_cu > 0 ? num_cu : 1;
             const int64_t t256x320 = (int64_t)((M + 255) / 256) * ((N + 319) / 320);
@@ -999,11 +1003,16 @@ TileShape choose_tile(GemmMode mode, int gs, int M, int N, int K, int num_cu)
             const double c160 = N % 160 == 0 ? rounds(t256x160) * (256.0 * 160.0) : 1e300;
             const double c256 = rounds(t256x128) * (256.0 * 128.0 / 0.9);
             const double c128 = rounds(t128x128) * (128.0 * 128.0 / 0.85);
-            if (c320 <= c160 && c320 <= c256 && c320 <= c128)
+            const int64_t t128x160 = (int64_t)((M + 127) / 128) * ((N + 159) / 160);
+            const double c160h = N % 160 == 0 ? rounds(t128x160) * (128.0 * 160.0 / 0.8) : 1e300;
+            const double best = std::min(std::min(c320, c160), std::min(std::min(c256, c128), c160h));
+            if (c320 == best)
                 return TileShape::T256x320w8;
-            if (c160 <= c256 && c160 <= c128)
+            if (c160 == best)
                 return TileShape::T256x160;
-            if (c256 <= c128)
+            if (c160h == best)
+                return TileShape::T128x160;
+            if (c256 == best)
                 return TileShape::T256x128;
             return TileShape::T128x128;
         }
@@ -1033,6 +1042,7 @@ TileInfo tile_dims(TileShape t)
     case TileShape::T256x128: r.bm = 256; r.bn = 128; r.waves = 4; break;
     case TileShape::T256x128w8: r.bm = 256; r.bn = 128; r.waves = 8; break;
     case TileShape::T256x160: r.bm = 256; r.bn = 160; r.waves = 4; break;
+    case TileShape::T128x160: r.bm = 128; r.bn = 160; r.waves = 4; break;
     case TileShape::T256x320w8: r.bm = 256; r.bn = 320; r.waves = 8; break;
     case TileShape::TSkinny: r.bm = 0; r.bn = 0; r.waves = 4; break;   // depends on M and N
     }

@@ -40,7 +40,8 @@ void launch_gemm(GemmMode mode, const GemmArgs &a, hipStream_t st);
 // Tile configurations of the GEMM kernel (BM x BN per workgroup; "w8" = eight
 // waves, i.e. two per SIMD, where the default is four).
 enum class TileShape : int {
-    T32x32, T32x128, T64x64, T64x128, T128x128, T128x128w8, T256x128, T256x128w8, T256x160,
+    T32x32, T32x128, T64x64, T64x128, T128x128, T128x128w8, T128x160, T256x128, T256x128w8,
+    T256x160,
     T256x320w8,  // the per-channel kernel of its own (K % 128 == 0)
     TSkinny      // per-channel, few tokens: weight rows per workgroup, K split over its waves
 };
