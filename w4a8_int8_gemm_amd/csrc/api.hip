@@ -479,11 +479,12 @@ w4a8_status_t w8a8_mv_pg(const w4a8_f16 *x, const int8_t *wq, const float *w_sca
         return st;
     if (N == 0)
         return ok();
-    st = check_device();
+    int cu = 0;
+    st = check_device(&cu);
     if (st != W4A8_OK)
         return st;
     launch_mv_group(false, group_size, x, reinterpret_cast<const uint8_t *>(wq), w_scale, y,
-                    (int)N, (int)K, (hipStream_t)stream);
+                    (int)N, (int)K, cu, (hipStream_t)stream);
     return check_launch("w8a8_mv_pg");
 }
 
@@ -496,10 +497,11 @@ w4a8_status_t w4a8_mv(const w4a8_f16 *x, const uint8_t *w4, const float *w_scale
         return st;
     if (N == 0)
         return ok();
-    st = check_device();
+    int cu = 0;
+    st = check_device(&cu);
     if (st != W4A8_OK)
         return st;
-    launch_mv_group(true, group_size, x, w4, w_scale, y, (int)N, (int)K, (hipStream_t)stream);
+    launch_mv_group(true, group_size, x, w4, w_scale, y, (int)N, (int)K, cu, (hipStream_t)stream);
     return check_launch("w4a8_mv");
 }
 

@@ -86,8 +86,9 @@ void launch_int8_mv(const uint16_t *x, const int8_t *w, const float *sw, uint16_
 
 // Decode matrix-vector with per-group weight scales: per-group W8A8 (token
 // quantized per group of gs) or W4A8 (packed int4 weights, per-token scale).
+// num_cu sizes the rows per workgroup.
 void launch_mv_group(bool int4, int gs, const uint16_t *x, const uint8_t *w, const float *sw,
-                     uint16_t *y, int N, int K, hipStream_t st);
+                     uint16_t *y, int N, int K, int num_cu, hipStream_t st);
 
 // Weight-only int8 comparison GEMM: y = fp16(w_scale[n] * sum_k x[m,k] wq[n,k])
 // with fp16 activations on the fp16 matrix cores (K % 64 == 0).

@@ -338,28 +338,41 @@ void launch_group(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t
 }
 
 // 16 lanes per row (16 rows per workgroup, so the token's quantization is
-// shared by 16 rows at any K); chunks in flight per lane by the row's
-// 16-byte chunks (rows longer than 256 chunks take several passes); token
-// chunks per thread by K.
-template <bool INT4, int GS>
-void launch_group_k(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
+// shared by 16 rows at any K) while that gives at least two workgroups per
+// compute unit; fewer int8 rows take 64 lanes per row (4 rows per
+// workgroup), so that every compute unit still has several row streams in
+// flight (measured: 4096 x 14336 16.7 us instead of 19.5; int4 rows, whose
+// chunks carry twice the codes, lost 25-35 % that way and keep 16 lanes).  Chunks in flight per lane by the row's 16-byte chunks (rows longer
+// than LPR * 16 chunks take several passes); token chunks per thread by K.
+template <bool INT4, int GS, int LPR>
+void launch_group_l(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
                     int K, hipStream_t st)
 {
     const int nch = (INT4 ? K / 2 : K) / 16;
     if (K <= 4096) {
-        if (nch <= 64)
-            launch_group<INT4, GS, 16, 4, 2>(x, w, sw, y, N, K, st);
-        else if (nch <= 128)
-            launch_group<INT4, GS, 16, 8, 2>(x, w, sw, y, N, K, st);
+        if (nch <= LPR * 4)
+            launch_group<INT4, GS, LPR, 4, 2>(x, w, sw, y, N, K, st);
+        else if (nch <= LPR * 8)
+            launch_group<INT4, GS, LPR, 8, 2>(x, w, sw, y, N, K, st);
         else
-            launch_group<INT4, GS, 16, 16, 2>(x, w, sw, y, N, K, st);
+            launch_group<INT4, GS, LPR, 16, 2>(x, w, sw, y, N, K, st);
     } else if (K <= 8192) {
-        launch_group<INT4, GS, 16, 16, 4>(x, w, sw, y, N, K, st);
+        launch_group<INT4, GS, LPR, 16, 4>(x, w, sw, y, N, K, st);
     } else if (K <= 16384) {
-        launch_group<INT4, GS, 16, 16, 8>(x, w, sw, y, N, K, st);
+        launch_group<INT4, GS, LPR, 16, 8>(x, w, sw, y, N, K, st);
     } else {
-        launch_group<INT4, GS, 16, 16, 16>(x, w, sw, y, N, K, st);
+        launch_group<INT4, GS, LPR, 16, 16>(x, w, sw, y, N, K, st);
     }
+}
+
+template <bool INT4, int GS>
+void launch_group_k(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
+                    int K, int cu, hipStream_t st)
+{
+    if (INT4 || N >= 16 * 2 * cu)
+        launch_group_l<INT4, GS, 16>(x, w, sw, y, N, K, st);
+    else
+        launch_group_l<INT4, GS, 64>(x, w, sw, y, N, K, st);
 }
 
 }  // namespace
@@ -660,12 +673,13 @@ void launch_few_w4(const int8_t *xq, const float *xs, const uint8_t *w, const fl
 }
 
 void launch_mv_group(bool int4, int gs, const uint16_t *x, const uint8_t *w, const float *sw,
-                     uint16_t *y, int N, int K, hipStream_t st)
+                     uint16_t *y, int N, int K, int num_cu, hipStream_t st)
 {
+    const int cu = num_cu > 0 ? num_cu : 1;
     if (int4)
-        (gs == 64 ? launch_group_k<true, 64> : launch_group_k<true, 128>)(x, w, sw, y, N, K, st);
+        (gs == 64 ? launch_group_k<true, 64> : launch_group_k<true, 128>)(x, w, sw, y, N, K, cu, st);
     else
-        (gs == 64 ? launch_group_k<false, 64> : launch_group_k<false, 128>)(x, w, sw, y, N, K, st);
+        (gs == 64 ? launch_group_k<false, 64> : launch_group_k<false, 128>)(x, w, sw, y, N, K, cu, st);
 }
 
 }  // namespace w4a8
