@@ -145,19 +145,23 @@ void launch_x(const uint16_t *x, const int8_t *w, const float *sw, uint16_t *y, 
 }
 
 
-// fp32 sum over groups of `width` consecutive lanes (16 or 64), with the
-// DPP moves of lane_reduce on the bit patterns (a lane a move does not reach
-// takes +0).
+// fp32 sum over groups of `width` consecutive lanes (16, 32 or 64), with
+// the DPP moves of lane_reduce on the bit patterns (a lane a move does not
+// reach takes +0).  The sum is in every lane of the group at widths 16 and
+// 64, and in the group's upper 16 lanes at width 32 (so the group's last lane
+// always holds it).
 template <int width>
 __device__ __forceinline__ float group_sum_f32(float v)
 {
 #define W4A8_DPPF(x, ctrl, rows) \
     __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctrl), (rows), 0xf, false))
-    static_assert(width == 16 || width == 64, "reduction width");
+    static_assert(width == 16 || width == 32 || width == 64, "reduction width");
     v += W4A8_DPPF(v, 0xb1, 0xf);
     v += W4A8_DPPF(v, 0x4e, 0xf);
     v += W4A8_DPPF(v, 0x141, 0xf);
     v += W4A8_DPPF(v, 0x140, 0xf);
+    if constexpr (width == 32)
+        v += W4A8_DPPF(v, 0x142, 0xa);             // row_bcast:15: rows 0, 2 into rows 1, 3
     if constexpr (width == 64) {
         v += W4A8_DPPF(v, 0x142, 0xa);
         v += W4A8_DPPF(v, 0x143, 0xc);
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restric
         }
     }
     acc = group_sum_f32<LPR>(acc);
-    if (lr == 0 && n < N)
+    if (lr == LPR - 1 && n < N)
         y[n] = f2h(INT4 ? acc * (s * 0.0625f) : acc);
 }
 
@@ -339,10 +343,11 @@ void launch_group(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t
 
 // 16 lanes per row (16 rows per workgroup, so the token's quantization is
 // shared by 16 rows at any K) while that gives at least two workgroups per
-// compute unit; fewer int8 rows take 64 lanes per row (4 rows per
+// compute unit; fewer rows take 64 lanes per row (int8; 4 rows per
+// workgroup) or 32 (int4, whose chunks carry twice the codes; 8 rows per
 // workgroup), so that every compute unit still has several row streams in
-// flight (measured: 4096 x 14336 16.7 us instead of 19.5; int4 rows, whose
-// chunks carry twice the codes, lost 25-35 % that way and keep 16 lanes).  Chunks in flight per lane by the row's 16-byte chunks (rows longer
+// flight (measured: int8 4096 x 14336 16.7 us instead of 19.5; int4 rows
+// lost 25-35 % at 64 lanes).  Chunks in flight per lane by the row's 16-byte chunks (rows longer
 // than LPR * 16 chunks take several passes); token chunks per thread by K.
 template <bool INT4, int GS, int LPR>
 void launch_group_l(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
@@ -369,8 +374,10 @@ template <bool INT4, int GS>
 void launch_group_k(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
                     int K, int cu, hipStream_t st)
 {
-    if (INT4 || N >= 16 * 2 * cu)
+    if (N >= 16 * 2 * cu)
         launch_group_l<INT4, GS, 16>(x, w, sw, y, N, K, st);
+    else if (INT4)
+        launch_group_l<INT4, GS, 32>(x, w, sw, y, N, K, st);
     else
         launch_group_l<INT4, GS, 64>(x, w, sw, y, N, K, st);
 }
