@@ -247,8 +247,11 @@ typedef enum {
 
 /* For a call of `op` with these sizes on the current device, writes
  *   out[0] = rows of the output tile a workgroup computes (0: the call runs
- *            the few-token matrix-vector form instead of the tiled GEMM),
- *   out[1] = columns of that tile,
+ *            the few-token matrix-vector form instead of the tiled GEMM; the
+ *            row-range forms for a few to a few hundred tokens: the tokens a
+ *            workgroup takes, padded),
+ *   out[1] = columns of that tile (row-range forms: the weight rows a
+ *            workgroup takes in one pass, padded to 16),
  *   out[2] = wavefronts per workgroup,
  *   out[3] = workgroups launched (the grid is persistent: at most as many as
  *            the device holds at once; each walks its share of the tiles),

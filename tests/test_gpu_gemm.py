@@ -3,9 +3,12 @@ bit, fp16 outputs within tolerance, against the oracle on the same seeded
 int8 codes and scales (drawn by the input generator, not by either side).
 
 Shapes are chosen to exercise every tile configuration the library selects
-(32x32, 64x64, 64x128, 128x128, 128x160, 256x128, 256x160, 256x320, and the few-token
+(32x32, 64x64, 64x128, 128x128, 128x160, 256x128, 256x160, 256x320, the few-token
 row-range form with each of its token paddings 16/32/64/128, one or several
-passes over a workgroup's rows, and workgroups with no K to do), ragged M/N
+passes over a workgroup's rows, and workgroups with no K to do, and the
+row-range form with shared stages for 33-256 tokens with one and two token
+slices, one and two token blocks per wave, workgroups without rows and K
+stages fewer than its ring holds), ragged M/N
 edges, N not a multiple of 4 (scalar stores), and K with a half-filled last
 stage (K % 128 == 64); test_tile_selection asserts which configuration the
 shapes the tests rely on run (gemm_tile_config)."""
@@ -65,6 +68,13 @@ PC_SHAPES = [
     # per workgroup; M * K at 65536 (last one on this path) and just above
     (2, 1001, 1024), (4, 333, 2048), (3, 10240, 2560), (1, 4099, 4096), (4, 777, 16384),
     (2, 5, 32768), (4, 129, 16448), (3, 4099, 14336), (4, 4096, 12288),
+    # 33-256 tokens, the row-range form with shared stages: 33-48 tokens at
+    # N > 8192 (N ragged against the 8-row units and not a multiple of 4,
+    # three stages against a ring of eight), up to 128 tokens at N <= 8192
+    # (two token slices), K >= 8192 up to 256 tokens (two blocks of 16 tokens
+    # per wave), N = 129 (most workgroups have no rows)
+    (33, 10240, 2560), (47, 10243, 384), (77, 3001, 1280), (128, 8192, 4096),
+    (200, 1030, 8192), (256, 2000, 8192), (40, 129, 256),
 ]
 
 
@@ -92,11 +102,21 @@ EXPECTED_TILES = {
     (5, 10240, 2560): (16, 48, 4),         # 40 rows per workgroup
     (32, 10240, 2560): (32, 48, 4),
     (8, 49160, 256): (16, 128, 4),         # 192 rows per workgroup: two passes
-    (100, 8192, 2560): (128, 32, 4),       # 32 rows per workgroup
-    (128, 4096, 4096): (128, 16, 4),
     (7, 5, 64): (16, 16, 4),
     (24, 40000, 192): (32, 128, 4),        # 160 rows per workgroup: two passes
-    (64, 10240, 2560): (64, 64, 2),        # 33-128 tokens with N > 8192: tiles
+    (65, 6150, 320): (128, 32, 4),         # K % 128 != 0: not the shared-stage form
+    (64, 10240, 2560): (64, 64, 2),        # 49-256 tokens with N > 8192 and K < 8192: tiles
+    (128, 10240, 2560): (64, 128, 4),
+    # 33-256 tokens, the row-range form with shared stages (the tokens of a
+    # slice padded to 64 per block per wave, the rows of a range padded to 16)
+    (33, 10240, 2560): (64, 48, 4),        # one slice, 40 rows per workgroup
+    (100, 8192, 2560): (64, 64, 4),        # two slices of 50 tokens, 64 rows
+    (128, 4096, 4096): (64, 32, 4),
+    (128, 8192, 4096): (64, 64, 4),
+    (77, 3001, 1280): (64, 32, 4),
+    (200, 1030, 8192): (128, 16, 4),       # two slices of 100 tokens
+    (256, 2000, 8192): (128, 16, 4),
+    (40, 129, 256): (64, 16, 4),
 }
 
 
@@ -218,12 +238,14 @@ def test_extreme_int8_codes(torch_gpu, oracle):
     assert_equal(host(w.w8a8_gemm_i32(dev(xq), dev(wq))), c_ref, "int32 sums")
 
 
-def test_largest_k_extreme_codes(torch_gpu, oracle):
+@pytest.mark.parametrize("M", [32, 40])
+def test_largest_k_extreme_codes(torch_gpu, oracle, M):
     """K = 133120, the largest multiple of 64 the per-channel entry points
     accept (127^2 K < 2^31): all-+-127 codes put the int32 sums within 0.02 %
-    of the int32 limit, through the int32 export and the fp16 epilogue."""
+    of the int32 limit, through the int32 export and the fp16 epilogue (32
+    tokens: the K-split row-range form; 40: the shared-stage one)."""
     import w4a8_int8_gemm_amd as w
-    M, N, K = 32, 64, 133120
+    N, K = 64, 133120
     xq = np.full((M, K), 127, np.int8)
     xq[1::2] = -127
     wq = np.full((N, K), 127, np.int8)

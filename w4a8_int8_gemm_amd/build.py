@@ -20,8 +20,8 @@ OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libw4a8.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_pc.hip", "gemm_skinny.hip", "mv.hip",
-           "w8a16.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_pc.hip", "gemm_skinny.hip", "gemm_rows.hip",
+           "mv.hip", "w8a16.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

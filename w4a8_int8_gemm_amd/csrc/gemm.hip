@@ -874,6 +874,7 @@ template <GemmMode MODE, int GS> constexpr bool tile_ok(TileShape t)
     case TileShape::T128x160: return !T::pergroup;
     case TileShape::T256x320w8: return false;       // a kernel of its own
     case TileShape::TSkinny: return false;          // a kernel of its own
+    case TileShape::TRows: return false;            // a kernel of its own
     }
     return false;
 }
@@ -900,6 +901,7 @@ int with_tile(TileShape t, A &&...args)
         W4A8_TILE(T128x160, 128, 160, 4, 1)
     case TileShape::T256x320w8:
     case TileShape::TSkinny:
+    case TileShape::TRows:
         return -1;
     }
 #undef W4A8_TILE
@@ -925,6 +927,8 @@ void launch_mode(const GemmArgs &a, hipStream_t st)
         launch_gemm_pc2(MODE == GemmMode::I32, a, st, true);
     else if (t == TileShape::TSkinny)
         launch_gemm_skinny(MODE == GemmMode::I32, a, st, true);
+    else if (t == TileShape::TRows)
+        launch_gemm_rows(MODE == GemmMode::I32, a, st, true);
     else
         with_tile<MODE, GS, LaunchCfgF>(t, a, st);
 }
@@ -944,6 +948,8 @@ TileInfo info_mode(const GemmArgs &a)
         return launch_gemm_pc2(MODE == GemmMode::I32, a, nullptr, false);
     if (t == TileShape::TSkinny)
         return launch_gemm_skinny(MODE == GemmMode::I32, a, nullptr, false);
+    if (t == TileShape::TRows)
+        return launch_gemm_rows(MODE == GemmMode::I32, a, nullptr, false);
     TileInfo r = tile_dims(t);
     const int64_t tiles = (int64_t)((a.M + r.bm - 1) / r.bm) * ((a.N + r.bn - 1) / r.bn);
     r.per_cu = resident_groups<MODE, GS>(t);
@@ -970,11 +976,25 @@ TileShape choose_tile(GemmMode mode, int gs, int M, int N, int K, int num_cu)
     const int64_t t256x160 = (int64_t)((M + 255) / 256) * ((N + 159) / 160);
     const int64_t t256x128 = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
     const int64_t t128x128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    // Tens to hundreds of tokens per channel: the product is bound by moving
+    // bytes.  The row-range form with shared stages (one compute unit per
+    // weight-row range and token slice) measured faster than the alternatives
+    // for 33-48 tokens (N=10240, K=2560: 9.4 against 10.5 us on 64x64 tiles),
+    // where the output is too narrow for enough tiles (N <= 8192, up to 128
+    // tokens: 128x8192x4096 13.8 against 15.1 us, 100x4096x14336 26 against
+    // 30 us, against the K-split form below), and for long rows (K >= 8192, up
+    // to 256 tokens: 256x4096x14336 36 against 39 us, 43 against 54 us with
+    // the weights from HBM).  At N=10240, K=2560 from 64 tokens on the tiles
+    // win (128 tokens: 10.0 against 12.3 us).
+    if (!pergroup && M > 32 && M <= 256 && (M <= 48 || K >= 8192 || (M <= 128 && N <= 8192)) &&
+        plan_gemm_rows(M, N, K, num_cu).ok)
+        return TileShape::TRows;
     // Few tokens per channel: the product is bound by one pass over the
-    // weights, and the row-range form (each compute unit streams a range of
-    // weight rows against all tokens) measured faster up to 32 tokens, and up
-    // to 128 where the output is too narrow (N <= 8192) for enough tiles.
-    // Every compute unit reads all of X, so beyond that the tiles win.
+    // weights, and the row-range form that splits K over its waves (each
+    // compute unit streams a range of weight rows against all tokens)
+    // measured faster up to 32 tokens, and up to 128 where the output is too
+    // narrow (N <= 8192) for enough tiles and K % 128 != 0.  Every compute
+    // unit reads all of X, so beyond that the tiles win.
     if (!pergroup && (M <= 32 || (M <= 128 && N <= 8192)))
         return TileShape::TSkinny;
     // Few tokens: the weights are streamed once and the output is small, so
@@ -1045,6 +1065,7 @@ TileInfo tile_dims(TileShape t)
     case TileShape::T128x160: r.bm = 128; r.bn = 160; r.waves = 4; break;
     case TileShape::T256x320w8: r.bm = 256; r.bn = 320; r.waves = 8; break;
     case TileShape::TSkinny: r.bm = 0; r.bn = 0; r.waves = 4; break;   // depends on M and N
+    case TileShape::TRows: r.bm = 0; r.bn = 0; r.waves = 4; break;     // depends on M and N
     }
     return r;
 }

@@ -43,7 +43,8 @@ enum class TileShape : int {
     T32x32, T32x128, T64x64, T64x128, T128x128, T128x128w8, T128x160, T256x128, T256x128w8,
     T256x160,
     T256x320w8,  // the per-channel kernel of its own (K % 128 == 0)
-    TSkinny      // per-channel, few tokens: weight rows per workgroup, K split over its waves
+    TSkinny,     // per-channel, few tokens: weight rows per workgroup, K split over its waves
+    TRows        // per-channel, tens to hundreds of tokens: weight rows per workgroup, shared stages
 };
 struct TileInfo {
     int bm, bn, waves;    // output tile per workgroup and its wavefronts
@@ -67,6 +68,24 @@ TileInfo launch_gemm_pc2(bool i32_out, const GemmArgs &a, hipStream_t st, bool l
 // each workgroup streams a contiguous range of weight rows against all tokens.
 // Its TileInfo gives bm = the tokens padded to 16, bn = the rows of one pass.
 TileInfo launch_gemm_skinny(bool i32_out, const GemmArgs &a, hipStream_t st, bool launch);
+
+// The per-channel (or raw int32) GEMM for tens to hundreds of tokens
+// (K % 128 == 0): one workgroup per compute unit streams a contiguous range of
+// weight rows against one or two slices of the tokens, whose four waves share
+// 128-byte K stages in a deep LDS ring.  plan_gemm_rows gives its split (ok is
+// false where it does not apply: more than 128 tokens per slice or 128 rows
+// per range); TileInfo gives bm = the tokens of a slice padded to 64, bn = the
+// rows of a range padded to 16.
+struct RowsPlan {
+    bool ok;
+    int pm;       // token slices (1 or 2)
+    int mbw;      // token blocks of 16 per wave (1 or 2)
+    int rb;       // row blocks of 16 per workgroup (1 .. 8)
+    int grid;     // workgroups (one per compute unit, a multiple of 8)
+    int units;    // weight rows in units of 8
+};
+RowsPlan plan_gemm_rows(int M, int N, int K, int num_cu);
+TileInfo launch_gemm_rows(bool i32_out, const GemmArgs &a, hipStream_t st, bool launch);
 
 // Few-token per-channel product (1 <= M <= 4, M * K <= 64 KiB): the weight
 // rows streamed whole against the tokens' codes in LDS; equals the

@@ -16,8 +16,9 @@ namespace w4a8 {
 
 namespace {
 
-// Per-token, row held in registers: CPL 16-byte chunks per lane (K <= 512*CPL).
-template <int CPL>
+// Per-token, row held in registers: CPL 16-byte chunks per lane (K <= 512*CPL;
+// FULL: K == 512*CPL, every lane's chunks exist and need no bounds checks).
+template <int CPL, bool FULL>
 __global__ __launch_bounds__(256) void quant_token_kernel(const uint16_t *__restrict__ x,
                                                           int8_t *__restrict__ q,
                                                           float *__restrict__ scale,
@@ -34,7 +35,10 @@ __global__ __launch_bounds__(256) void quant_token_kernel(const uint16_t *__rest
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = lane + 64 * j;
-        v[j] = (c < nch) ? load_nt(xr + c) : make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (FULL)
+            v[j] = load_nt(xr + c);
+        else
+            v[j] = (c < nch) ? load_nt(xr + c) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
@@ -49,7 +53,7 @@ __global__ __launch_bounds__(256) void quant_token_kernel(const uint16_t *__rest
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = lane + 64 * j;
-        if (c < nch)
+        if (FULL || c < nch)
             qr[c] = quant_chunk8(v[j], s, r, qmax);
     }
 }
@@ -127,8 +131,12 @@ void launch_token(const uint16_t *x, int8_t *q, float *s, int64_t rows, int K, f
                   hipStream_t st)
 {
     const unsigned blocks = (unsigned)((rows + 3) / 4);
-    hipLaunchKernelGGL(quant_token_kernel<CPL>, dim3(blocks), dim3(256), 0, st, x, q, s, rows, K,
-                       qmax);
+    if (K == 512 * CPL)
+        hipLaunchKernelGGL((quant_token_kernel<CPL, true>), dim3(blocks), dim3(256), 0, st, x, q,
+                           s, rows, K, qmax);
+    else
+        hipLaunchKernelGGL((quant_token_kernel<CPL, false>), dim3(blocks), dim3(256), 0, st, x, q,
+                           s, rows, K, qmax);
 }
 
 }  // namespace
