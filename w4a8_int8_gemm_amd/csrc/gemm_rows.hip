@@ -17,12 +17,13 @@
 //    row range sit on one XCD (one L2), so the weights still come from HBM
 //    once.
 //  * K advances in stages of 128 bytes -- whole 128-byte lines of every row
-//    -- through a ring of D stages in LDS (D = 5 to 8: as many as about
+//    -- through a ring of D stages in LDS (D = 4 to 8: as many as about
 //    144 KiB hold), copied from global memory straight into LDS.  The four
 //    waves share every stage: each copies a quarter of its 1 KiB blocks (8 rows
-//    of 128 bytes), and one barrier per stage publishes it.  With D - 2 later
-//    stages in flight, a compute unit keeps 70-120 KiB of loads outstanding,
-//    which the HBM latency needs.
+//    of 128 bytes), and one barrier per stage publishes it.  With D - 3 later
+//    stages in flight, a compute unit keeps 50-100 KiB of loads outstanding,
+//    which the HBM latency needs.  A stage's fragments are read from LDS one
+//    iteration ahead, beside the MFMAs of the stage before.
 //  * The waves split the tokens (MBW blocks of 16 each) and take all rows
 //    (RB blocks of 16): v_mfma_i32_16x16x64_i8 with the weights as the first
 //    operand, two k-steps per stage.  A lane of the result holds one token and
@@ -76,7 +77,8 @@ void gemm_rows_kernel(GemmArgs args, int units, int pm_slices, int i32_out)
     const int pm = local % pm_slices;
     const int ranges = G / pm_slices;
     const int pn = xcd * (per_xcd / pm_slices) + local / pm_slices;
-    const int u0 = (int)((int64_t)units * pn / ranges), u1 = (int)((int64_t)units * (pn + 1) / ranges);
+    const int u0 = (int)((int64_t)units * pn / ranges);
+    const int u1 = (int)((int64_t)units * (pn + 1) / ranges);
     const int r_begin = 8 * u0, r_end = min(N, 8 * u1);
     const int m_slice = (M + pm_slices - 1) / pm_slices;
     const int m_begin = pm * m_slice, m_end = min(M, m_begin + m_slice);
@@ -132,43 +134,68 @@ void gemm_rows_kernel(GemmArgs args, int units, int pm_slices, int i32_out)
         for (int mb = 0; mb < MBW; ++mb)
             acc[rb][mb] = v4i{0, 0, 0, 0};
 
-    auto compute = [&](int slot) __attribute__((always_inline)) {
+    // the fragments of one stage: both k-steps, tokens then rows
+    struct Frag {
+        v4i x[2][MBW], w[2][RB];
+    };
+    auto read_frags = [&](Frag &F, int slot) __attribute__((always_inline)) {
         const int8_t *base = ring + slot * STAGE;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            v4i xa[MBW], wa[RB];
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb)
-                xa[mb] = *reinterpret_cast<const v4i *>(base + ((wave * MBW + mb) * 16) * RSK + fo[h]);
+                F.x[h][mb] =
+                    *reinterpret_cast<const v4i *>(base + ((wave * MBW + mb) * 16) * RSK + fo[h]);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                wa[rb] = *reinterpret_cast<const v4i *>(base + (XR + rb * 16) * RSK + fo[h]);
+                F.w[h][rb] = *reinterpret_cast<const v4i *>(base + (XR + rb * 16) * RSK + fo[h]);
+        }
+    };
+    auto compute = [&](const Frag &F) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int mb = 0; mb < MBW; ++mb)
-                    acc[rb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[rb], xa[mb], acc[rb][mb],
-                                                                        0, 0, 0);
-        }
+                    acc[rb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(F.w[h][rb], F.x[h][mb],
+                                                                        acc[rb][mb], 0, 0, 0);
     };
 
-    // ---- pipeline.  Stages 0 .. D-2 are issued up front.  Iteration s waits
-    // for its own copies of stage s (the D-2 later stages stay in flight),
-    // barriers -- stage s is visible and every wave is done with stage s-1 --
-    // issues stage s+D-1 into the slot stage s-1 vacated, and computes stage s.
+    // ---- pipeline.  Stages 0 .. D-2 are issued up front and stage 0's
+    // fragments read.  Iteration s waits for its own copies of stage s+1 (the
+    // D-3 later stages stay in flight), barriers -- stage s+1 is visible and
+    // every wave is done with stage s-1, whose fragments it read an iteration
+    // earlier -- issues stage s+D-1 into the slot stage s-1 vacated, reads
+    // stage s+1's fragments and computes stage s from the fragments read in
+    // the previous iteration, so the LDS reads run beside the MFMAs.
+    static_assert(D >= 3, "ring depth");
 #pragma unroll
     for (int t = 0; t < D - 1; ++t)
         issue_stage(t, t);
-    int slot = 0;
-    for (int s = 0; s < nstage; ++s) {
+    Frag f0, f1;
+    wait_vmcnt<(D - 2) * NCW>();
+    lds_barrier();
+    read_frags(f0, 0);
+    int slot = 0;                                     // slot of stage s
+    auto iteration = [&](int s, Frag &cur, Frag &nxt) __attribute__((always_inline)) {
+        const int nslot = slot == D - 1 ? 0 : slot + 1;
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<(D - 2) * NCW>();
+        wait_vmcnt<(D - 3) * NCW>();
         lds_barrier();
         issue_stage(slot == 0 ? D - 1 : slot - 1, s + D - 1);
         __builtin_amdgcn_sched_barrier(0);
-        compute(slot);
-        slot = slot == D - 1 ? 0 : slot + 1;
+        read_frags(nxt, nslot);                       // past the last stage: zeros, unused
+        compute(cur);
+        slot = nslot;
+    };
+    int s = 0;
+    for (; s + 2 <= nstage; s += 2) {
+        iteration(s, f0, f1);
+        iteration(s + 1, f1, f0);
     }
+    if (s < nstage)
+        iteration(s, f0, f1);
     // no copy may still be writing LDS when the workgroup ends
     wait_vmcnt<0>();
 
