@@ -106,8 +106,9 @@ def kernel_sample():
     HBM-bound kernels: quantize_act per token (4096x2560) and per group
     (4096x4096, gs 128 and 64), and the decode matrix-vector kernels
     (int8_mv 10240x2560, w8a8_mv_pg 14336x4096 gs=128, w4a8_mv 24576x4096),
-    and the few-token per-channel and W4A8 products (w8a8_gemm_pc at M = 2
-    and 4, 10240x2560; w4a8_gemm gs=128 at M = 2 and 4, 24576x4096), each
+    the few-token per-channel and W4A8 products (w8a8_gemm_pc at M = 2
+    and 4, 10240x2560; w4a8_gemm gs=128 at M = 2 and 4, 24576x4096) and the
+    shared-stage row-range GEMM (128x8192x4096, 256x4096x14336), each
     three times with a 1 GiB buffer written before every call so the
     weights come from HBM.  Meant to run under `rocprofv3 --pmc`
     (a few dispatches per kernel)."""
@@ -191,6 +192,20 @@ def kernel_sample():
         torch.cuda.synchronize()
         del x, xq, xs, y
     del wq, sw
+    # tens to hundreds of tokens: the shared-stage row-range GEMM
+    for (M, N, K) in [(128, 8192, 4096), (256, 4096, 14336)]:
+        log(f"kernel sample: per-channel row-range M={M} N={N} K={K}")
+        wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
+        wq, sw = w.quantize_weight_int8(wt, 0)
+        del wt
+        x = torch.from_numpy(synth.activations(M, K, seed=1)).cuda()
+        xq, xs = w.quantize_act(x, 0)
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        for _ in range(3):
+            flush.fill_(1)
+            w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y), M, N, K, sp))
+        torch.cuda.synchronize()
+        del x, xq, xs, y, wq, sw
     N, K, gs = 24576, 4096, 128
     wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
     wq, sw = w.pack_weight_int4(wt, gs)
@@ -426,6 +441,38 @@ def suite(reps, with_oracle=True):
             print(rows[-1], flush=True)
             del x, y, wq, sw, xq, xs
             torch.cuda.empty_cache()
+    # tens to hundreds of tokens per channel outside the workload list, where
+    # the shared-stage row-range GEMM runs (and the 128-token row of the
+    # N=10240 layer, on tiles, beside them): the GEMM warm, then cold for the
+    # kernel trace (a 1 GiB buffer written before every call)
+    for (M, N, K) in [(33, 10240, 2560), (128, 8192, 4096), (100, 4096, 14336),
+                      (256, 4096, 14336)]:
+        x = torch.from_numpy(synth.activations(M, K, seed=1)).cuda()
+        wt = torch.from_numpy(synth.weights(N, K, seed=2)).cuda()
+        wq, sw = w.quantize_weight_int8(wt, 0)
+        del wt
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        xq, xs = w.quantize_act(x, 0)
+        g = lambda: w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y), M, N, K,
+                                           sp))
+        gus = b2b(g)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for _ in range(reps):
+            flush.fill_(1)
+            g()
+        torch.cuda.synchronize()
+        del flush
+        t = w.gemm_tile_config(w.GemmOp.GEMM_PC, M, N, K)
+        nbytes = N * K + M * K + 2 * M * N + 4 * (M + N)
+        ops = 2.0 * M * N * K
+        rows.append(f"pc_tokens  M={M:5d} N={N:5d} K={K:5d}  gemm {gus:8.2f} us warm "
+                    f"({t['bm']}x{t['bn']}, {t['waves']} waves, {t['grid']} workgroups) "
+                    f"{ops / gus / 1e6:7.1f} TOPS | {nbytes / gus / 1e3:6.0f} GB/s "
+                    f"({100 * nbytes / gus / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak, "
+                    f"{100 * nbytes / gus / 1e3 / copy_gbs:.0f}% of the copy rate)")
+        print(rows[-1], flush=True)
+        del x, y, wq, sw, xq, xs
+        torch.cuda.empty_cache()
     # decode (M = 1) with per-group weight scales: the matrix-vector kernels,
     # warm and (for the kernel trace) cold, against quantize_act + the mode's
     # GEMM at M = 1

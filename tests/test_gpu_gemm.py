@@ -157,6 +157,27 @@ def test_gemm_i32_and_pc(torch_gpu, oracle, M, N, K):
     assert stats["exact_frac"] > 0.99, stats
 
 
+# Few to a few hundred tokens at the N=10240, K=2560 layer with N made ragged
+# (10243: not a multiple of 8 or 4), through every form the dispatch picks on
+# the way: the few-token matrix-vector form of the fp16 product (1) and the
+# K-split row-range form (the int32 export at 1; 5, 8), the shared-stage
+# row-range form (33), 64x64 tiles (64) and 64x128 tiles (128, 200, 256); int32
+# sums bit for bit and fp16 against the oracle.
+@pytest.mark.parametrize("M", [1, 5, 8, 33, 64, 128, 200, 256])
+def test_tokens_sweep_ragged_n(torch_gpu, oracle, M):
+    import w4a8_int8_gemm_amd as w
+    N, K = 10243, 2560
+    print(f"gemm pc token sweep M={M} N={N} K={K}", flush=True)
+    seed = 7 * M + 1
+    xq, wq = synth.int8_codes(M, K, seed, 0), synth.int8_codes(N, K, seed, 1)
+    sa, sw = synth.scales(M, 0, seed, 0, 3.0), synth.scales(N, 0, seed, 1)
+    c_ref = oracle.gemm_i32(xq, wq)
+    assert_equal(host(w.w8a8_gemm_i32(dev(xq), dev(wq))), c_ref, "int32 sums")
+    y = w.w8a8_gemm_pc(dev(xq), dev(sa), dev(wq), dev(sw))
+    stats = assert_fp16_close(host(y), oracle.epilogue_pc(c_ref, sa, sw), what="fp16 y")
+    assert stats["exact_frac"] > 0.99, stats
+
+
 # The last three reach the 256x128 two-waves-per-SIMD tiles (>= 384 tiles);
 # 1800x6100 is ragged in both M and N, and K = 448 leaves a 64-wide K tail
 # (gs = 64 only).
