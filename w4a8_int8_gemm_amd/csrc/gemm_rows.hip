@@ -30,9 +30,10 @@
 //    four consecutive rows, the output's 8-byte runs.
 //  * Chunk c of LDS row r sits at c ^ (r & 7) ^ ((r >> 3) & 1): the 16 rows one
 //    fragment read serves per cycle hit distinct banks.
-//  * Workgroups start their K loop at different stages (the sum is exact in
-//    any order), so that the compute units of an XCD do not all ask for the
-//    same lines of the activations at once.
+//  * The row ranges of an XCD start their K loop at different stages (the sum
+//    is exact in any order), so that its compute units do not all ask for the
+//    same lines of the activations at once; the token slices of one range
+//    start at the same stage, so the weights stay a single HBM stream.
 //  * Rows past the range, tokens past the slice and stages past the end read
 //    as zeros (buffer resources sized to the valid bytes).  K % 128 == 0.
 //  * The epilogue is the tiled GEMM's rescale, so the fp16 outputs equal the
@@ -83,8 +84,10 @@ void gemm_rows_kernel(GemmArgs args, int units, int pm_slices, int i32_out)
     const int m_slice = (M + pm_slices - 1) / pm_slices;
     const int m_begin = pm * m_slice, m_end = min(M, m_begin + m_slice);
     const int nstage = K / RSK;
-    // K start: a multiple of 4 stages apart within an XCD
-    const int rot = (4 * local) % nstage;
+    // K start: row ranges of an XCD a multiple of 4 stages apart; the token
+    // slices of one range start together, so the second asks for the same
+    // weight lines as the first while they are still in L2
+    const int rot = (4 * (local / pm_slices)) % nstage;
 
     const v4i rx = make_rsrc(args.xq + (int64_t)m_begin * K,
                              (uint32_t)(max(0, m_end - m_begin) * K));
