@@ -289,7 +289,7 @@ RowsPlan plan_gemm_rows(int M, int N, int K, int num_cu)
     p.ok = false;
     // one workgroup per compute unit, a multiple of 8 (one per XCD slot)
     const int grid = (num_cu / 8) * 8;
-    if (grid < 8 || K % RSK != 0 || M < 1)
+    if (grid < 8 || K < RSK || K % RSK != 0 || M < 1 || N < 1)
         return p;
     const int units = (N + 7) / 8;
     int best = 0;
