@@ -331,8 +331,12 @@ def suite(reps, with_oracle=True):
     and quantize + GEMM of the per-channel M=128 and M=4096 shapes, are also
     run cold (a 1 GiB buffer written before every call, so inputs come from
     HBM rather than the 256 MB Infinity Cache); run under
-    `rocprofv3 --kernel-trace` for those per-dispatch durations.  Each
-    back-to-back timing follows 25 ms of untimed calls of the same kernel."""
+    `rocprofv3 --kernel-trace` for those per-dispatch durations.  The kernels
+    bound by moving bytes (the M=1 kernels, the M=128 per-channel GEMM, the
+    tens-to-hundreds-of-tokens GEMMs) also get a cold figure of their own
+    from events: a batch of (read a 1 GiB buffer, call) pairs less a batch
+    of the reads alone, per call.  Each back-to-back timing follows 25 ms of
+    untimed calls of the same kernel."""
     import numpy as np
     import torch
 
@@ -351,6 +355,26 @@ def suite(reps, with_oracle=True):
     copy_gbs = copy_rate_gbs()
     print(f"device copy rate (512 MiB copy, read + write): {copy_gbs:.0f} GB/s "
           f"({100 * copy_gbs / PEAK_HBM_GBS:.0f}% of HBM peak)", flush=True)
+
+    # cold: the weights from HBM.  A 1 GiB buffer is read (a max over it,
+    # no dirty lines left behind) before every call; the time of a batch of
+    # such pairs minus that of the reads alone, per call, median of 5 batches
+    flush_src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros((), dtype=torch.uint8, device="cuda")
+
+    def cold(fn, n=20):
+        def batch(with_call):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(n):
+                sink.copy_(flush_src.amax())
+                if with_call:
+                    fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+        batch(True)
+        return float(np.median([batch(True) - batch(False) for _ in range(5)]))
 
     def b2b(fn):
         fn()
@@ -398,9 +422,11 @@ def suite(reps, with_oracle=True):
                 torch.cuda.synchronize()
                 del flush
                 wbytes = N * K + 2 * K + 6 * N
+                cus = cold(fn)
                 rows.append(f"{name:10s} M={M:5d} N={N:5d} K={K:5d}  int8_mv {us:8.2f} us warm  "
                             f"{wbytes / us / 1e3:7.0f} GB/s ({100 * wbytes / us / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak, "
-                            f"{100 * wbytes / us / 1e3 / copy_gbs:.0f}% of the copy rate)")
+                            f"{100 * wbytes / us / 1e3 / copy_gbs:.0f}% of the copy rate) | cold {cus:7.2f} us "
+                            f"{wbytes / cus / 1e3:7.0f} GB/s ({100 * wbytes / cus / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak)")
                 continue
             q = lambda: w.check(L.quantize_act(ptr(x), M, K, act_gs, ptr(xq), ptr(xs), sp))
             if mode == "pc":
@@ -433,11 +459,18 @@ def suite(reps, with_oracle=True):
                 valu_us = M * N * (K // gs) * FOLD_VALU_OPS[mode] / PEAK_VALU_OPS * 1e6
                 bound = (f" | bound max(MFMA {mfma_us:.1f}, VALU fold {valu_us:.1f}) us: "
                          f"{100 * max(mfma_us, valu_us) / gus:4.1f}% of it")
+            cold_txt = ""
+            if mode == "pc" and M == 128:
+                # bound by moving bytes: the GEMM with the weights from HBM too
+                gbytes = N * K + M * K + 2 * M * N + 4 * (M + N)
+                cg = cold(g)
+                cold_txt = (f" | gemm cold {cg:7.2f} us {gbytes / cg / 1e3:6.0f} GB/s "
+                            f"({100 * gbytes / cg / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak)")
             rows.append(f"{name:10s} M={M:5d} N={N:5d} K={K:5d}  quantize {qus:7.2f} us "
                         f"({qbytes / qus / 1e3:5.0f} GB/s, {100 * qbytes / qus / 1e3 / copy_gbs:3.0f}% of copy rate)"
                         f" | gemm {gus:8.2f} us "
                         f"{ops / gus / 1e6:7.1f} TOPS ({100 * ops / gus / 1e6 / PEAK_INT8_TOPS:4.1f}% "
-                        f"of int8 peak){bound} | step {ops / (qus + gus) / 1e6:7.1f} TOPS")
+                        f"of int8 peak){bound} | step {ops / (qus + gus) / 1e6:7.1f} TOPS{cold_txt}")
             print(rows[-1], flush=True)
             del x, y, wq, sw, xq, xs
             torch.cuda.empty_cache()
@@ -465,11 +498,13 @@ def suite(reps, with_oracle=True):
         t = w.gemm_tile_config(w.GemmOp.GEMM_PC, M, N, K)
         nbytes = N * K + M * K + 2 * M * N + 4 * (M + N)
         ops = 2.0 * M * N * K
+        cg = cold(g)
         rows.append(f"pc_tokens  M={M:5d} N={N:5d} K={K:5d}  gemm {gus:8.2f} us warm "
                     f"({t['bm']}x{t['bn']}, {t['waves']} waves, {t['grid']} workgroups) "
                     f"{ops / gus / 1e6:7.1f} TOPS | {nbytes / gus / 1e3:6.0f} GB/s "
                     f"({100 * nbytes / gus / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak, "
-                    f"{100 * nbytes / gus / 1e3 / copy_gbs:.0f}% of the copy rate)")
+                    f"{100 * nbytes / gus / 1e3 / copy_gbs:.0f}% of the copy rate) | cold {cg:7.2f} us "
+                    f"{nbytes / cg / 1e3:6.0f} GB/s ({100 * nbytes / cg / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak)")
         print(rows[-1], flush=True)
         del x, y, wq, sw, xq, xs
         torch.cuda.empty_cache()
@@ -509,9 +544,12 @@ def suite(reps, with_oracle=True):
         del flush
         wbytes = wq.numel() + sw.numel() * 4 + 2 * K + 2 * N
         kern = "w4a8_mv" if mode == "w4a8" else "w8a8_mv_pg"
+        cus = cold(mv)
         rows.append(f"{mode + '_mv':10s} M=    1 N={N:5d} K={K:5d}  {kern} gs={gs} {us:8.2f} us warm  "
                     f"{wbytes / us / 1e3:7.0f} GB/s ({100 * wbytes / us / 1e3 / PEAK_HBM_GBS:.0f}% "
                     f"of HBM peak, {100 * wbytes / us / 1e3 / copy_gbs:.0f}% of the copy rate) | "
+                    f"cold {cus:7.2f} us {wbytes / cus / 1e3:7.0f} GB/s "
+                    f"({100 * wbytes / cus / 1e3 / PEAK_HBM_GBS:.0f}% of HBM peak) | "
                     f"quantize + GEMM at M=1 {path_us:8.2f} us")
         print(rows[-1], flush=True)
         del x, y, wq, sw, xq, xs
