@@ -38,14 +38,19 @@ __global__ __launch_bounds__(256) void int8_mv_kernel(const uint16_t *__restrict
     const bool row_ok = n < N;
     const uint4 *wr = reinterpret_cast<const uint4 *>(w + (int64_t)min(n, N - 1) * K);
 
-    // 1. this thread's chunks of the token (8 fp16 each): c = tid + 256 j
+    // 1. this thread's chunks of the token (8 fp16 each): c = tid + 256 j.
+    // Indexes past the end are clamped to the last chunk, whose value then
+    // goes unused (a repeated chunk leaves the amax as it is, and the codes
+    // and dot products below skip it): no load sits under a branch, since a
+    // branch around a load makes the compiler wait for every load in flight
+    // where the paths join, and the token would then wait for the weights.
     const uint4 *xr = reinterpret_cast<const uint4 *>(x);
     const int nx = K >> 3;
     uint4 xv[XCH];
 #pragma unroll
     for (int j = 0; j < XCH; ++j) {
         const int c = tid + 256 * j;
-        xv[j] = c < nx ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+        xv[j] = xr[min(c, nx - 1)];
     }
 
     // 2. first batch of weight loads in flight
@@ -53,8 +58,11 @@ __global__ __launch_bounds__(256) void int8_mv_kernel(const uint16_t *__restrict
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = lr + LPR * j;
-        wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+        wv[j] = load_nt(wr + min(c, nch - 1));
     }
+
+    // every load above is issued before any of the token's data is used
+    __builtin_amdgcn_sched_barrier(0);
 
     // 3. the token's amax (reduction over the workgroup)
     uint32_t m = 0;
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(256) void int8_mv_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = next + lr + LPR * j;
-            wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+            wv[j] = load_nt(wr + min(c, nch - 1));
         }
     }
     acc = group_sum_i32<LPR>(acc);
@@ -209,14 +217,15 @@ __global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restric
     const float *swr = sw + (int64_t)min(n, N - 1) * G;    // the row's group scales
     const bool leader = lr % CPG == 0;              // first lane of its group's lanes
 
-    // 1. this thread's chunks of the token (8 fp16 each): c = tid + 256 j
+    // 1. this thread's chunks of the token (8 fp16 each): c = tid + 256 j,
+    // loads clamped to the last chunk as in the per-channel kernel
     const uint4 *xr = reinterpret_cast<const uint4 *>(x);
     const int nx = K >> 3;
     uint4 xv[XCH];
 #pragma unroll
     for (int j = 0; j < XCH; ++j) {
         const int c = tid + 256 * j;
-        xv[j] = c < nx ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+        xv[j] = xr[min(c, nx - 1)];
     }
 
     // 2. first batch of weight loads in flight, with the group scales the
@@ -226,13 +235,15 @@ __global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restric
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = lr + LPR * j;
-        wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+        wv[j] = load_nt(wr + min(c, nch - 1));
     }
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = lr + LPR * j;
-        swv[j] = (leader && c < nch) ? swr[c / CPG] : 0.0f;
+        swv[j] = swr[min(c, nch - 1) / CPG];
     }
+
+    __builtin_amdgcn_sched_barrier(0);
 
     // 3. the token's scale(s) and codes
     float s = 0.0f;                                 // the token's scale (int4)
@@ -317,12 +328,12 @@ __global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restric
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = next + lr + LPR * j;
-            wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+            wv[j] = load_nt(wr + min(c, nch - 1));
         }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = next + lr + LPR * j;
-            swv[j] = (leader && c < nch) ? swr[c / CPG] : 0.0f;
+            swv[j] = swr[min(c, nch - 1) / CPG];
         }
     }
     acc = group_sum_f32<LPR>(acc);
