@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256) void int8_mv_kernel(const uint16_t *__restrict
         const int c = lr + LPR * j;
         wv[j] = load_nt(wr + min(c, nch - 1));
     }
+    const float swn = sw[min(n, N - 1)];            // the row's scale, for the rescale
 
     // every load above is issued before any of the token's data is used
     __builtin_amdgcn_sched_barrier(0);
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void int8_mv_kernel(const uint16_t *__restrict
     }
     acc = group_sum_i32<LPR>(acc);
     if (lr == 0 && row_ok)
-        y[n] = f2h(rescale_pc(acc, s, sw[n]));
+        y[n] = f2h(rescale_pc(acc, s, swn));
 }
 
 template <int LPR, int CPL, int XCH>
@@ -438,17 +439,48 @@ __global__ __launch_bounds__(256) void few_pc_kernel(const int8_t *__restrict__ 
         n[r] = blockIdx.x * (RPB * RPT) + r * RPB + tid / LPR;
         wr[r] = reinterpret_cast<const uint4 *>(w + (int64_t)min(n[r], N - 1) * K);
     }
+    // Loads in the order their data is needed (they complete in issue order):
+    // the tokens' codes (held in registers while K <= 4096, i.e. at most MT
+    // chunks per thread), then the weight rows, then the scales for the
+    // rescale.  Indexes past the end are clamped and their values unused, so
+    // that no load sits under a branch (the compiler would wait for every
+    // load in flight where the paths join).
+    const int xch = (M * K) >> 4;
+    // (native vector type: a struct copy would be folded into a memcpy at
+    // the LDS store, after the weight loads)
+    const v4u *xq4 = reinterpret_cast<const v4u *>(xq);
+    constexpr int XQ = LPR == 16 ? MT : 1;
+    v4u xqv[XQ];
+    if constexpr (LPR == 16) {
+#pragma unroll
+        for (int j = 0; j < XQ; ++j)
+            xqv[j] = xq4[min(tid + 256 * j, xch - 1)];
+    }
     uint4 wv[RPT][CPL];
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = lr + LPR * j;
-            wv[r][j] = (c < nch) ? load_nt(wr[r] + c) : make_uint4(0u, 0u, 0u, 0u);
+            wv[r][j] = load_nt(wr[r] + min(c, nch - 1));
         }
-    const int xch = (M * K) >> 4;
-    for (int c = tid; c < xch; c += 256)
-        reinterpret_cast<uint4 *>(xq_s)[c] = reinterpret_cast<const uint4 *>(xq)[c];
+    float swn[RPT], xsv[MT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        swn[r] = sw[min(n[r], N - 1)];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        xsv[t] = xs[min(t, M - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (LPR == 16) {
+        // a clamped index stores the last chunk's own value again
+#pragma unroll
+        for (int j = 0; j < XQ; ++j)
+            reinterpret_cast<v4u *>(xq_s)[min(tid + 256 * j, xch - 1)] = xqv[j];
+    } else {
+        for (int c = tid; c < xch; c += 256)
+            reinterpret_cast<v4u *>(xq_s)[c] = xq4[c];
+    }
     __syncthreads();
 
     int acc[RPT][MT];
@@ -486,18 +518,17 @@ __global__ __launch_bounds__(256) void few_pc_kernel(const int8_t *__restrict__ 
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int c = next + lr + LPR * j;
-                wv[r][j] = (c < nch) ? load_nt(wr[r] + c) : make_uint4(0u, 0u, 0u, 0u);
+                wv[r][j] = load_nt(wr[r] + min(c, nch - 1));
             }
     }
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-        const float swn = sw[min(n[r], N - 1)];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             if (t < M) {
                 const int a = group_sum_i32<LPR>(acc[r][t]);
                 if (lr == 0 && n[r] < N)
-                    y[(int64_t)t * N + n[r]] = f2h(rescale_pc(a, xs[t], swn));
+                    y[(int64_t)t * N + n[r]] = f2h(rescale_pc(a, xsv[t], swn[r]));
             }
         }
     }
@@ -544,25 +575,54 @@ __global__ __launch_bounds__(256) void few_w4_kernel(const int8_t *__restrict__ 
     const float *swr = sw + (int64_t)min(n, N - 1) * G;
     const bool leader = lr % CPG == 0;
 
+    // Loads in the order their data is needed, none under a branch (as in
+    // the per-channel few-token kernel): the tokens' codes, 8 k at a time
+    // (in registers while K <= 4096: at most 2 MT pieces per thread), the
+    // weight rows, their group scales and the tokens' scales.
+    const int x8 = (M * K) >> 3;
+    const uint2 *xq2 = reinterpret_cast<const uint2 *>(xq);
+    constexpr bool XREG = CPL <= 8;                 // K <= 4096
+    constexpr int XQ = XREG ? 2 * MT : 1;
+    uint2 xqv[XQ];
+    if constexpr (XREG) {
+#pragma unroll
+        for (int j = 0; j < XQ; ++j)
+            xqv[j] = xq2[min(tid + 256 * j, x8 - 1)];
+    }
     uint4 wv[CPL];
     float swv[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = lr + LPR * j;
-        wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+        wv[j] = load_nt(wr + min(c, nch - 1));
     }
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = lr + LPR * j;
-        swv[j] = (leader && c < nch) ? swr[c / CPG] : 0.0f;
+        swv[j] = swr[min(c, nch - 1) / CPG];
     }
-    // the tokens' codes, 8 k at a time: (even k, odd k)
-    const int x8 = (M * K) >> 3;
-    for (int c = tid; c < x8; c += 256) {
-        const uint2 q = reinterpret_cast<const uint2 *>(xq)[c];
-        reinterpret_cast<uint2 *>(xq_s)[c] =
-            make_uint2(__builtin_amdgcn_perm(q.y, q.x, 0x06040200u),
-                       __builtin_amdgcn_perm(q.y, q.x, 0x07050301u));
+    float xsv[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        xsv[t] = xs[min(t, M - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    // the codes into LDS as (even k, odd k)
+    if constexpr (XREG) {
+        // a clamped index stores the last piece's own value again
+#pragma unroll
+        for (int j = 0; j < XQ; ++j) {
+            const uint2 q = xqv[j];
+            reinterpret_cast<uint2 *>(xq_s)[min(tid + 256 * j, x8 - 1)] =
+                make_uint2(__builtin_amdgcn_perm(q.y, q.x, 0x06040200u),
+                           __builtin_amdgcn_perm(q.y, q.x, 0x07050301u));
+        }
+    } else {
+        for (int c = tid; c < x8; c += 256) {
+            const uint2 q = xq2[c];
+            reinterpret_cast<uint2 *>(xq_s)[c] =
+                make_uint2(__builtin_amdgcn_perm(q.y, q.x, 0x06040200u),
+                           __builtin_amdgcn_perm(q.y, q.x, 0x07050301u));
+        }
     }
     __syncthreads();
 
@@ -603,12 +663,12 @@ __global__ __launch_bounds__(256) void few_w4_kernel(const int8_t *__restrict__ 
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = next + lr + LPR * j;
-            wv[j] = (c < nch) ? load_nt(wr + c) : make_uint4(0u, 0u, 0u, 0u);
+            wv[j] = load_nt(wr + min(c, nch - 1));
         }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = next + lr + LPR * j;
-            swv[j] = (leader && c < nch) ? swr[c / CPG] : 0.0f;
+            swv[j] = swr[min(c, nch - 1) / CPG];
         }
     }
 #pragma unroll
@@ -616,7 +676,7 @@ __global__ __launch_bounds__(256) void few_w4_kernel(const int8_t *__restrict__ 
         if (t < M) {
             const float a = group_sum_f32<LPR>(acc[t]);
             if (lr == 0 && n < N)
-                y[(int64_t)t * N + n] = f2h(a * (xs[t] * 0.0625f));
+                y[(int64_t)t * N + n] = f2h(a * (xsv[t] * 0.0625f));
         }
     }
 }
