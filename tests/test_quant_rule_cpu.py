@@ -23,6 +23,11 @@ def shim(tmp_path_factory):
     L.shim_quantize.argtypes = [fp, ctypes.c_int, ctypes.c_float, ctypes.c_float, i8p, fp]
     L.shim_quantize.restype = ctypes.c_int
     L.shim_fast_only.argtypes = [fp, ctypes.c_int, ctypes.c_float, ctypes.c_float, i8p]
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.shim_check_corrected.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_float, ip, ip]
+    L.shim_check_corrected.restype = ctypes.c_long
+    L.shim_count_uncorrected.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_float]
+    L.shim_count_uncorrected.restype = ctypes.c_long
     return L
 
 
@@ -75,3 +80,37 @@ def test_guard_is_needed(shim, oracle):
         if mismatches:
             break
     assert mismatches > 0
+
+
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_corrected_quotient_on_the_whole_domain(shim, qmax):
+    """The kernels' division-free quotient for guarded elements (reciprocal,
+    product, exact residual by fma, one correction) equals fl32(x / s) -- and
+    its code the division rule's -- for every fp16 amax (s = fl32(amax/qmax))
+    and every fp16 x with |x| <= amax, both signs: about 10^9 pairs, split
+    over threads (each ctypes call releases the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    # ranges of amax bits with about equal work (work grows with the bits)
+    top = 0x7C00
+    edges = [1]
+    for i in range(1, 64):
+        edges.append(int(top * (i / 64) ** 0.5))
+    edges.append(top)
+    edges = sorted(set(edges))
+
+    def run(k):
+        a, b = ctypes.c_int(-1), ctypes.c_int(-1)
+        n = shim.shim_check_corrected(edges[k], edges[k + 1], float(qmax), ctypes.byref(a),
+                                      ctypes.byref(b))
+        return n, a.value, b.value
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        results = list(ex.map(run, range(len(edges) - 1)))
+    bad = [(n, a, b) for n, a, b in results if n]
+    assert not bad, f"mismatches (count, first amax bits, first x bits): {bad[:3]}"
+
+
+def test_correction_step_is_needed(shim):
+    """Without the correction the product fl32(x r) misses fl32(x / s) on
+    part of the same domain, so the check above is a real one."""
+    assert shim.shim_count_uncorrected(0x3C00, 0x3C40, 127.0) > 0

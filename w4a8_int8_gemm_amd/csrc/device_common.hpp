@@ -130,39 +130,70 @@ __device__ __forceinline__ uint32_t low_bytes4(float a, float b, float c, float 
     return ab | cd;
 }
 
-// Quantize the eight fp16 values of a chunk with scale s (r = fl32(1/s)).
-// Fast path for all eight: t = fl32(x r); m = t + 1.5 * 2^23 rounds t to the
-// nearest integer (ties to even, |t| < 2^22) and holds it, two's complement,
-// in its low mantissa bits, so byte 0 of m is the code and m - 1.5 * 2^23
-// (exact) is rint(t) for the guard.  If any of the eight is guarded, the
-// whole chunk goes through the division rule.  Returns the codes as two
-// dwords.
-__device__ __forceinline__ uint2 quant_chunk8(uint4 v, float s, float r, float qmax)
+// Quantize the eight fp16 values of a chunk with scale s (r = fl32(1/s)),
+// in two parts (quant_chunk8 runs the first, and the second only when the
+// guard trips):
+//  * quant_chunk8_fast: t = fl32(x r); m = t + 1.5 * 2^23 rounds t to the
+//    nearest integer (ties to even, |t| < 2^22) and holds it, two's
+//    complement, in its low mantissa bits, so byte 0 of m is the code and
+//    m - 1.5 * 2^23 (exact) is rint(t); the largest distance |t - rint(t)|
+//    of the eight is folded into `far` for the guard;
+//  * quant_chunk8_div: the division rule's codes for all eight, from the
+//    corrected quotient q = fl32(x / s) (quant_div_corrected: no division
+//    instruction); q + 1.5 * 2^23 holds rint(q) in byte 0 as above, which is
+//    round_half_away(q) unless q is exactly a half-integer -- a chunk holding
+//    such a tie takes quant_code_corrected (roundf) for all eight.
+// A chunk whose distance trips the guard takes the division rule whole; a
+// zero scale (all-zero slice) gives zero codes.
+__device__ __forceinline__ uint2 quant_chunk8_fast(uint4 v, float r, float &far)
 {
-    if (s == 0.0f)
-        return make_uint2(0u, 0u);
     constexpr float kRound = 0x1.8p23f;
     const float t[8] = {h2f_times<false>(v.x, r), h2f_times<true>(v.x, r),
                         h2f_times<false>(v.y, r), h2f_times<true>(v.y, r),
                         h2f_times<false>(v.z, r), h2f_times<true>(v.z, r),
                         h2f_times<false>(v.w, r), h2f_times<true>(v.w, r)};
     float m[8];
-    float far = 0.0f;                 // largest distance to an integer
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         m[i] = t[i] + kRound;
         far = fmaxf(far, fabsf(t[i] - (m[i] - kRound)));
     }
-    if (__builtin_expect(quant_fast_slow(far), 0)) {
-        const float x[8] = {lo_h2f(v.x), hi_h2f(v.x), lo_h2f(v.y), hi_h2f(v.y),
-                            lo_h2f(v.z), hi_h2f(v.z), lo_h2f(v.w), hi_h2f(v.w)};
+    return make_uint2(low_bytes4(m[0], m[1], m[2], m[3]), low_bytes4(m[4], m[5], m[6], m[7]));
+}
+
+__device__ __forceinline__ uint2 quant_chunk8_div(uint4 v, float s, float r, float qmax)
+{
+    constexpr float kRound = 0x1.8p23f;
+    const float x[8] = {lo_h2f(v.x), hi_h2f(v.x), lo_h2f(v.y), hi_h2f(v.y),
+                        lo_h2f(v.z), hi_h2f(v.z), lo_h2f(v.w), hi_h2f(v.w)};
+    float m[8];
+    float tie = 0.0f;                 // largest |q - rint(q)|: 1/2 only for an exact tie
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float q = quant_div_corrected(x[i], s, r);
+        m[i] = q + kRound;
+        tie = fmaxf(tie, fabsf(q - (m[i] - kRound)));
+    }
+    if (__builtin_expect(tie == 0.5f, 0)) {
         int q[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            q[i] = quant_code_div(x[i], s, qmax);
+            q[i] = quant_code_corrected(x[i], s, r, qmax);
         return make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]));
     }
     return make_uint2(low_bytes4(m[0], m[1], m[2], m[3]), low_bytes4(m[4], m[5], m[6], m[7]));
+}
+
+// Both parts for one chunk, the guard tested per chunk.
+__device__ __forceinline__ uint2 quant_chunk8(uint4 v, float s, float r, float qmax)
+{
+    if (s == 0.0f)
+        return make_uint2(0u, 0u);
+    float far = 0.0f;
+    const uint2 c = quant_chunk8_fast(v, r, far);
+    if (__builtin_expect(quant_fast_slow(far), 0))
+        return quant_chunk8_div(v, s, r, qmax);
+    return c;
 }
 
 // Per-channel rescale of one int32 sum; the same operation order everywhere

@@ -7,15 +7,18 @@
 //     s = fl32(amax / qmax),  q = clamp(round_half_away(fl32(x / s)), -qmax, qmax)
 // with qmax = 127 (int8) or 7 (int4) and true IEEE fp32 division.
 //
-// Two ways to reach the same code:
+// Three ways to reach the same code:
 //  * quant_code_div: the rule as written (one IEEE division per element);
+//  * quant_code_corrected (below): the same quotient from the reciprocal and
+//    one fma correction, exact on the kernels' whole input domain;
 //  * quant_code_fast: t = fl32(x r) with r = fl32(1/s), code rint(t), plus a
 //    guard.  t differs from x/s by at most |x/s| 2^-23 (r and the product
 //    carry one rounding each), which is below 1.6e-5 for |x/s| <= 128, so
 //    rint(t) equals round_half_away(fl32(x/s)) unless x/s lies within that
 //    distance of a half-integer.  The guard flags every t whose distance to
 //    its nearest integer exceeds 1/2 - 2^-14 (exact ties included, where rint
-//    and round_half_away differ); those elements take quant_code_div.  The
+//    and round_half_away differ); those elements take quant_code_div (the
+//    kernels: quant_code_corrected, the same codes).  The
 //    clamp is never active on this path: with |x| <= amax (s is derived from
 //    the slice's own amax), |t| <= qmax (1 + 2^-22) < qmax + 1/2 - 2^-14.
 //    The test is split so a kernel can take the maximum distance over
@@ -46,6 +49,30 @@ W4A8_HD int quant_code_div(float x, float s, float qmax)
     float r = roundf(t);                       // halves go away from zero
     r = fminf(fmaxf(r, -qmax), qmax);
     return (int)r;
+}
+
+// The quotient fl32(x / s) without a division instruction, for the guarded
+// elements: with r = fl32(1/s) (correctly rounded) and t = fl32(x r), the
+// residual e = x - t s is computed exactly by one fma, and fl32(t + e r) is
+// the correctly rounded quotient (one correction step of the reciprocal
+// method).  The CPU test suite checks that it equals x / s bit for bit for
+// every fp16 x with |x| <= amax and every fp16 amax, s = fl32(amax / qmax),
+// qmax = 127 and 7: the whole domain the kernels use it on.  A short chain of
+// three dependent operations instead of the division's, whose latency sits
+// on the critical path of every wave that meets a guarded element.
+W4A8_HD float quant_div_corrected(float x, float s, float r)
+{
+    const float t = fmaf(x, r, -0.0f);
+    const float e = fmaf(-t, s, x);
+    return fmaf(e, r, t);
+}
+
+// The rule with that quotient (s != 0); equals quant_code_div on the domain above.
+W4A8_HD int quant_code_corrected(float x, float s, float r, float qmax)
+{
+    float q = roundf(quant_div_corrected(x, s, r));   // halves go away from zero
+    q = fminf(fmaxf(q, -qmax), qmax);
+    return (int)q;
 }
 
 // Guard width: v within this distance of an integer goes to the slow path.
