@@ -3,6 +3,7 @@
 // on every fp16 input.  Test code only.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "../../w4a8_int8_gemm_amd/csrc/quant_rule.h"
 
@@ -92,6 +93,20 @@ long shim_count_uncorrected(int lo, int hi, float qmax)
             const float x = h2f_bits((uint16_t)xb);
             bad += (x / s) != fmaf(x, r, -0.0f);
         }
+    }
+    return bad;
+}
+
+// quant_scale against the plain division for every non-negative fp16 amax
+// (zero, subnormals, normals, infinity): the number of bit-pattern mismatches.
+long shim_check_scale(float qmax)
+{
+    long bad = 0;
+    for (int ab = 0; ab <= 0x7C00; ++ab) {
+        const float amax = h2f_bits((uint16_t)ab);
+        const float want = amax / qmax;
+        const float got = w4a8::quant_scale(amax, qmax);
+        bad += memcmp(&want, &got, sizeof(float)) != 0;
     }
     return bad;
 }

@@ -28,6 +28,8 @@ def shim(tmp_path_factory):
     L.shim_check_corrected.restype = ctypes.c_long
     L.shim_count_uncorrected.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_float]
     L.shim_count_uncorrected.restype = ctypes.c_long
+    L.shim_check_scale.argtypes = [ctypes.c_float]
+    L.shim_check_scale.restype = ctypes.c_long
     return L
 
 
@@ -114,3 +116,10 @@ def test_correction_step_is_needed(shim):
     """Without the correction the product fl32(x r) misses fl32(x / s) on
     part of the same domain, so the check above is a real one."""
     assert shim.shim_count_uncorrected(0x3C00, 0x3C40, 127.0) > 0
+
+
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_scale_without_division_on_every_amax(shim, qmax):
+    """The kernels' scale (reciprocal of qmax, product, one fma correction)
+    equals fl32(amax / qmax) bit for bit for every non-negative fp16 amax."""
+    assert shim.shim_check_scale(float(qmax)) == 0

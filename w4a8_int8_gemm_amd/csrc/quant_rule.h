@@ -38,7 +38,20 @@
 
 namespace w4a8 {
 
-W4A8_HD float quant_scale(float amax, float qmax) { return amax / qmax; }
+// s = fl32(amax / qmax) without a division instruction: with c = fl32(1/qmax)
+// and s0 = fl32(amax c), one correction step fl32(s0 + (amax - s0 qmax) c)
+// (the residual exact by one fma) gives the quotient; the host test suite
+// checks it bit for bit against the division for every fp16 amax, infinity
+// included, at qmax = 127 and 7 -- the only values the kernels use.  An
+// infinite amax keeps the division's infinite scale (the correction would
+// turn it into NaN).
+W4A8_HD float quant_scale(float amax, float qmax)
+{
+    const float c = 1.0f / qmax;
+    const float s0 = amax * c;
+    const float s = fmaf(fmaf(-s0, qmax, amax), c, s0);
+    return s0 == INFINITY ? s0 : s;
+}
 
 // The rule as written.  s == 0 only for an all-zero slice, whose codes are 0.
 W4A8_HD int quant_code_div(float x, float s, float qmax)
