@@ -327,7 +327,8 @@ def oracle_timings(target_s=1.0):
 def suite(reps, with_oracle=True):
     """Per-workload kernel timings (not the JSON line): every shape of
     synth.WORKLOADS through its path, each kernel `reps` times back to back
-    between two events, through the C entry points.  The decode shapes (M=1),
+    between two events (the median of five such batches), through the C
+    entry points.  The decode shapes (M=1),
     and quantize + GEMM of the per-channel M=128 and M=4096 shapes, are also
     run cold (a 1 GiB buffer written before every call, so inputs come from
     HBM rather than the 256 MB Infinity Cache); run under
@@ -335,8 +336,8 @@ def suite(reps, with_oracle=True):
     bound by moving bytes (the M=1 kernels, the M=128 per-channel GEMM, the
     tens-to-hundreds-of-tokens GEMMs) also get a cold figure of their own
     from events: a batch of (read a 1 GiB buffer, call) pairs less a batch
-    of the reads alone, per call.  Each back-to-back timing follows 25 ms of
-    untimed calls of the same kernel."""
+    of the reads alone, per call (40 pairs, median of 9 batches).  Each
+    back-to-back timing follows 25 ms of untimed calls of the same kernel."""
     import numpy as np
     import torch
 
@@ -358,11 +359,11 @@ def suite(reps, with_oracle=True):
 
     # cold: the weights from HBM.  A 1 GiB buffer is read (a max over it,
     # no dirty lines left behind) before every call; the time of a batch of
-    # such pairs minus that of the reads alone, per call, median of 5 batches
+    # 40 such pairs minus that of the 40 reads alone, per call, median of 9
     flush_src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     sink = torch.zeros((), dtype=torch.uint8, device="cuda")
 
-    def cold(fn, n=20):
+    def cold(fn, n=40):
         def batch(with_call):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(st)
@@ -374,7 +375,7 @@ def suite(reps, with_oracle=True):
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) * 1e3 / n
         batch(True)
-        return float(np.median([batch(True) - batch(False) for _ in range(5)]))
+        return float(np.median([batch(True) - batch(False) for _ in range(9)]))
 
     def b2b(fn):
         fn()
@@ -386,13 +387,18 @@ def suite(reps, with_oracle=True):
             for _ in range(50):
                 fn()
             torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(reps):
-            fn()
-        e1.record(st)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
+        # median of five batches of `reps` calls (a single batch of a short
+        # kernel was seen 40 % off its steady rate)
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return float(np.median(times))
 
     rows = []
     for name, wl in synth.WORKLOADS.items():
