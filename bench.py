@@ -100,8 +100,9 @@ def counters_from_profiles():
 
 
 def kernel_sample():
-    """Three launches of each large GEMM kind, nothing else timed or printed
-    on stdout: the per-channel headline, per-group gs=128 and gs=64 at
+    """Launches of each large GEMM kind (20 to settle the clocks, then three
+    more), nothing else timed or printed on stdout: the per-channel headline,
+    per-group gs=128 and gs=64 at
     4096x14336x4096, and the W4A8 gate_up linear (4516x24576x4096); then the
     HBM-bound kernels: quantize_act per token (4096x2560) and per group
     (4096x4096, gs 128 and 64), and the decode matrix-vector kernels
@@ -136,7 +137,8 @@ def kernel_sample():
         else:
             wq, sw = w.quantize_weight_int8(wt, gs)
         xq, xs = w.quantize_act(x, gs if mode == "pg" else 0)
-        for _ in range(3):
+        # 20 launches to settle the clocks, then the three sampled ones
+        for _ in range(23):
             if mode == "pc":
                 w.check(L.w8a8_gemm_pc(ptr(xq), ptr(xs), ptr(wq), ptr(sw), ptr(y), M, N, K, sp))
             elif mode == "pg":
