@@ -15,8 +15,10 @@ def torch_gpu():
 
 QUANT_SHAPES = [
     (16, 256), (1, 2560), (37, 2560), (128, 2560), (3, 14336), (5, 16), (7, 8), (9, 520),
-    (2, 16384), (3, 20480),        # the two-pass kernel beyond register-resident rows
-    (4, 12288), (130, 4096),
+    (2, 16384), (3, 16000),        # the largest register-resident rows (full, ragged)
+    (4, 12288), (3, 12000),
+    (3, 20480), (2, 16392),        # the two-pass kernel beyond them
+    (130, 4096),
 ]
 
 

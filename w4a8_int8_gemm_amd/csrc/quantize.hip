@@ -158,6 +158,10 @@ void launch_quantize_rows(const uint16_t *x, int64_t rows, int K, int gs, float 
         case 7: case 8: launch_token<8>(x, q8, scale, rows, K, qmax, st); return;
         case 9: case 10: case 11: case 12: launch_token<12>(x, q8, scale, rows, K, qmax, st); return;
         case 13: case 14: case 15: case 16: launch_token<16>(x, q8, scale, rows, K, qmax, st); return;
+        case 17: case 18: case 19: case 20: case 21: case 22: case 23: case 24:
+            launch_token<24>(x, q8, scale, rows, K, qmax, st); return;
+        case 25: case 26: case 27: case 28: case 29: case 30: case 31: case 32:
+            launch_token<32>(x, q8, scale, rows, K, qmax, st); return;
         default:
             hipLaunchKernelGGL(quant_token_loop_kernel, dim3(blocks), dim3(256), 0, st, x, q8, scale,
                                rows, K, qmax);
