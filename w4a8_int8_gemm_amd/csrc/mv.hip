@@ -191,8 +191,8 @@ __device__ __forceinline__ float group_sum_f32(float v)
 // 16 * code (the nibble moved into the high half of a byte), so the token's
 // codes are staged split into even and odd k to meet the low and high
 // nibbles of each weight byte; the factor 16 is undone at the end (exact).
-template <bool INT4, int GS, int LPR, int CPL, int XCH>
-__global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restrict__ x,
+template <bool INT4, int GS, int LPR, int CPL, int XCH, int NT>
+__global__ __launch_bounds__(NT) void mv_group_kernel(const uint16_t *__restrict__ x,
                                                        const uint8_t *__restrict__ w,
                                                        const float *__restrict__ sw,
                                                        uint16_t *__restrict__ y, int N, int K)
@@ -200,8 +200,9 @@ __global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restric
     // LDS: the token's codes (K bytes), then its per-group scales (per-group
     // mode, K/GS floats)
     extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-    __shared__ uint32_t red[4];
-    constexpr int RPB = 256 / LPR;                  // rows per workgroup
+    constexpr int NW = NT / 64;                     // waves per workgroup
+    __shared__ uint32_t red[NW];
+    constexpr int RPB = NT / LPR;                   // rows per workgroup
     constexpr int KPC = INT4 ? 32 : 16;             // k per 16-byte weight chunk
     constexpr int CPG = GS / KPC;                   // chunks per group
     static_assert(CPG == 2 || CPG == 4 || CPG == 8, "chunks per group");
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restric
     uint4 xv[XCH];
 #pragma unroll
     for (int j = 0; j < XCH; ++j) {
-        const int c = tid + 256 * j;
+        const int c = tid + NT * j;
         xv[j] = xr[min(c, nx - 1)];
     }
 
@@ -257,12 +258,15 @@ __global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restric
         if (lane == 0)
             red[wave] = m;
         __syncthreads();
-        m = max(max(red[0], red[1]), max(red[2], red[3]));
+        m = red[0];
+#pragma unroll
+        for (int i = 1; i < NW; ++i)
+            m = max(m, red[i]);
         s = quant_scale(h2f((uint16_t)m), 127.0f);
         const float r = 1.0f / s;
 #pragma unroll
         for (int j = 0; j < XCH; ++j) {
-            const int c = tid + 256 * j;
+            const int c = tid + NT * j;
             if (c < nx) {
                 // k 8c .. 8c+7 -> (even k, odd k): the order of the low and
                 // high nibbles of the weight dword that covers them
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restric
         // groups of GS / 8 consecutive threads share a group of the token
 #pragma unroll
         for (int j = 0; j < XCH; ++j) {
-            const int c = tid + 256 * j;
+            const int c = tid + NT * j;
             const uint32_t m = group_max_u32<GS / 8>(absmax_bits8(xv[j]));
             const float sg = quant_scale(h2f((uint16_t)m), 127.0f);
             const float r = 1.0f / sg;
@@ -342,15 +346,43 @@ __global__ __launch_bounds__(256) void mv_group_kernel(const uint16_t *__restric
         y[n] = f2h(INT4 ? acc * (s * 0.0625f) : acc);
 }
 
-template <bool INT4, int GS, int LPR, int CPL, int XCH>
+template <bool INT4, int GS, int LPR, int CPL, int XCH, int NT = 256>
 void launch_group(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
                   int K, hipStream_t st)
 {
-    constexpr int RPB = 256 / LPR;
+    constexpr int RPB = NT / LPR;
     const unsigned blocks = (unsigned)((N + RPB - 1) / RPB);
     const size_t lds = (size_t)K + sizeof(float) * (INT4 ? 0 : K / GS);
-    hipLaunchKernelGGL((mv_group_kernel<INT4, GS, LPR, CPL, XCH>), dim3(blocks), dim3(256), lds,
+    hipLaunchKernelGGL((mv_group_kernel<INT4, GS, LPR, CPL, XCH, NT>), dim3(blocks), dim3(NT), lds,
                        st, x, w, sw, y, N, K);
+}
+
+// 512-thread workgroups (twice the rows per workgroup, so the
+// token is quantized half as often and each thread quantizes half as many
+// of its chunks).  Taken for int4 where the workgroups then fit one round
+// over the compute units, and for int8 rows up to K = 8192 (measured, warm /
+// cold µs: int4 4096 x 12288 9.4 / 10.8 -> 8.4 / 9.1, int8 gs=128 4096 x
+// 4096 5.0 / 4.5 -> 4.5 / 3.9, 6144 x 4096 6.1 -> 5.4 warm; int4 at 6144 rows,
+// 1.5 workgroups per compute unit, ran 5-25 % slower; int8 at K = 14336 4 %).
+template <bool INT4, int GS, int LPR>
+void launch_group_l512(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
+                       int K, hipStream_t st)
+{
+    const int nch = (INT4 ? K / 2 : K) / 16;
+    if (K <= 4096) {
+        if (nch <= LPR * 4)
+            launch_group<INT4, GS, LPR, 4, 1, 512>(x, w, sw, y, N, K, st);
+        else if (nch <= LPR * 8)
+            launch_group<INT4, GS, LPR, 8, 1, 512>(x, w, sw, y, N, K, st);
+        else
+            launch_group<INT4, GS, LPR, 16, 1, 512>(x, w, sw, y, N, K, st);
+    } else if (K <= 8192) {
+        launch_group<INT4, GS, LPR, 16, 2, 512>(x, w, sw, y, N, K, st);
+    } else if (K <= 16384) {
+        launch_group<INT4, GS, LPR, 16, 4, 512>(x, w, sw, y, N, K, st);
+    } else {
+        launch_group<INT4, GS, LPR, 16, 8, 512>(x, w, sw, y, N, K, st);
+    }
 }
 
 // 16 lanes per row (16 rows per workgroup, so the token's quantization is
@@ -388,8 +420,12 @@ void launch_group_k(const uint16_t *x, const uint8_t *w, const float *sw, uint16
 {
     if (N >= 16 * 2 * cu)
         launch_group_l<INT4, GS, 16>(x, w, sw, y, N, K, st);
+    else if (INT4 && (N + 15) / 16 <= cu)
+        launch_group_l512<INT4, GS, 32>(x, w, sw, y, N, K, st);
     else if (INT4)
         launch_group_l<INT4, GS, 32>(x, w, sw, y, N, K, st);
+    else if (K <= 8192)
+        launch_group_l512<INT4, GS, 64>(x, w, sw, y, N, K, st);
     else
         launch_group_l<INT4, GS, 64>(x, w, sw, y, N, K, st);
 }
