@@ -17,9 +17,10 @@ def torch_gpu():
 
 # (N, K): 4, 8 and 16 weight chunks in flight per lane, rows of several
 # passes, 2, 4, 8 and 16 token chunks per thread, N not a multiple of the 16
-# rows per workgroup, the smallest and the largest K
+# rows per workgroup, the smallest and the largest K; 5000 and 6100 rows take
+# the 768-thread int4 workgroups on a 256-CU device
 SHAPES = [(300, 1024), (129, 2048), (4096, 4096), (1000, 8192), (4096, 14336), (77, 32768),
-          (17, 128)]
+          (17, 128), (5000, 4096), (6100, 8192)]
 
 
 @pytest.mark.parametrize("gs", [64, 128])

@@ -357,32 +357,33 @@ void launch_group(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t
                        st, x, w, sw, y, N, K);
 }
 
-// 512-thread workgroups (twice the rows per workgroup, so the
-// token is quantized half as often and each thread quantizes half as many
-// of its chunks).  Taken for int4 where the workgroups then fit one round
-// over the compute units, and for int8 rows up to K = 8192 (measured, warm /
-// cold µs: int4 4096 x 12288 9.4 / 10.8 -> 8.4 / 9.1, int8 gs=128 4096 x
-// 4096 5.0 / 4.5 -> 4.5 / 3.9, 6144 x 4096 6.1 -> 5.4 warm; int4 at 6144 rows,
-// 1.5 workgroups per compute unit, ran 5-25 % slower; int8 at K = 14336 4 %).
-template <bool INT4, int GS, int LPR>
-void launch_group_l512(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
-                       int K, hipStream_t st)
+// Workgroups of NT = 512 or 768 threads (2-3x the rows of a 256-thread
+// workgroup, so the token is quantized that much less often and each thread
+// quantizes fewer of its chunks).  Taken for int4 where the workgroups then
+// fit one round over the compute units, and for int8 rows up to K = 8192
+// (measured, warm / cold us: int4 4096 x 12288 9.4 / 10.8 -> 8.4 / 9.1 at 512
+// threads, int4 6144 x 4096 5.1 / 5.0 -> 4.5 / 4.9 at 768, int8 gs=128 4096 x
+// 4096 5.0 / 4.5 -> 4.5 / 3.9 and 6144 x 4096 6.1 -> 5.4 warm at 512; int4 at
+// 6144 rows with 512 threads, 1.5 workgroups per compute unit, ran 5-25 %
+// slower, int8 at K = 14336 4 % slower).  Token chunks per thread by K.
+template <bool INT4, int GS, int LPR, int NT>
+void launch_group_nt(const uint16_t *x, const uint8_t *w, const float *sw, uint16_t *y, int N,
+                     int K, hipStream_t st)
 {
     const int nch = (INT4 ? K / 2 : K) / 16;
-    if (K <= 4096) {
-        if (nch <= LPR * 4)
-            launch_group<INT4, GS, LPR, 4, 1, 512>(x, w, sw, y, N, K, st);
-        else if (nch <= LPR * 8)
-            launch_group<INT4, GS, LPR, 8, 1, 512>(x, w, sw, y, N, K, st);
-        else
-            launch_group<INT4, GS, LPR, 16, 1, 512>(x, w, sw, y, N, K, st);
-    } else if (K <= 8192) {
-        launch_group<INT4, GS, LPR, 16, 2, 512>(x, w, sw, y, N, K, st);
-    } else if (K <= 16384) {
-        launch_group<INT4, GS, LPR, 16, 4, 512>(x, w, sw, y, N, K, st);
-    } else {
-        launch_group<INT4, GS, LPR, 16, 8, 512>(x, w, sw, y, N, K, st);
-    }
+    const int xch = (K / 8 + NT - 1) / NT;
+    if (nch <= LPR * 4 && xch <= 1)
+        launch_group<INT4, GS, LPR, 4, 1, NT>(x, w, sw, y, N, K, st);
+    else if (nch <= LPR * 8 && xch <= 1)
+        launch_group<INT4, GS, LPR, 8, 1, NT>(x, w, sw, y, N, K, st);
+    else if (xch <= 1)
+        launch_group<INT4, GS, LPR, 16, 1, NT>(x, w, sw, y, N, K, st);
+    else if (xch <= 2)
+        launch_group<INT4, GS, LPR, 16, 2, NT>(x, w, sw, y, N, K, st);
+    else if (xch <= 4)
+        launch_group<INT4, GS, LPR, 16, 4, NT>(x, w, sw, y, N, K, st);
+    else
+        launch_group<INT4, GS, LPR, 16, 8, NT>(x, w, sw, y, N, K, st);
 }
 
 // 16 lanes per row (16 rows per workgroup, so the token's quantization is
@@ -421,11 +422,13 @@ void launch_group_k(const uint16_t *x, const uint8_t *w, const float *sw, uint16
     if (N >= 16 * 2 * cu)
         launch_group_l<INT4, GS, 16>(x, w, sw, y, N, K, st);
     else if (INT4 && (N + 15) / 16 <= cu)
-        launch_group_l512<INT4, GS, 32>(x, w, sw, y, N, K, st);
+        launch_group_nt<INT4, GS, 32, 512>(x, w, sw, y, N, K, st);
+    else if (INT4 && (N + 23) / 24 <= cu)
+        launch_group_nt<INT4, GS, 32, 768>(x, w, sw, y, N, K, st);
     else if (INT4)
         launch_group_l<INT4, GS, 32>(x, w, sw, y, N, K, st);
     else if (K <= 8192)
-        launch_group_l512<INT4, GS, 64>(x, w, sw, y, N, K, st);
+        launch_group_nt<INT4, GS, 64, 512>(x, w, sw, y, N, K, st);
     else
         launch_group_l<INT4, GS, 64>(x, w, sw, y, N, K, st);
 }
