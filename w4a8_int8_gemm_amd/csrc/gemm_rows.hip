@@ -28,8 +28,14 @@
 //    (RB blocks of 16): v_mfma_i32_16x16x64_i8 with the weights as the first
 //    operand, two k-steps per stage.  A lane of the result holds one token and
 //    four consecutive rows, the output's 8-byte runs.
-//  * Chunk c of LDS row r sits at c ^ (r & 7) ^ ((r >> 3) & 1): the 16 rows one
-//    fragment read serves per cycle hit distinct banks.
+//  * Chunk c of LDS row r sits at c ^ (r & 7) ^ ((r >> 3) & 1).  A 16-byte LDS
+//    read serves 16 lanes a cycle: per half-wave, those whose 4-lane quad
+//    index (lane bits 2-4) has one parity, as the LDS bank-conflict counter
+//    shows -- rows 0-3 and 12-15 of a fragment from one lane group and rows
+//    4-11 from the next.  Lanes 0-15, 16-31, 32-47, 48-63 take the k chunks
+//    4h, 4h + 2, 4h + 1, 4h + 3 of k-step h (any order serves the product if
+//    both operands use it): two chunks 2 apart put those 16 reads in distinct
+//    banks, where chunks 1 apart would meet in half of them.
 //  * The row ranges of an XCD start their K loop at different stages (the sum
 //    is exact in any order), so that its compute units do not all ask for the
 //    same lines of the activations at once; the token slices of one range
@@ -123,12 +129,14 @@ void gemm_rows_kernel(GemmArgs args, int units, int pm_slices, int i32_out)
     };
 
     // ---- fragments: lane l reads row l%16 of a 16-row block, logical chunk
-    // 4h + l/16 for k-step h (blocks start at multiples of 16 rows)
+    // 4h + g for k-step h, g = 0, 2, 1, 3 for lane groups l/16 = 0 .. 3
+    // (blocks start at multiples of 16 rows)
     const int frow = lane & 15;
+    const int fg = (((lane >> 4) & 1) << 1) | (lane >> 5);
     int fo[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-        fo[h] = frow * RSK + 16 * rswz(frow, 4 * h + (lane >> 4));
+        fo[h] = frow * RSK + 16 * rswz(frow, 4 * h + fg);
 
     v4i acc[RB][MBW];
 #pragma unroll

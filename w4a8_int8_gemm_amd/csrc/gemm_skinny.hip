@@ -23,12 +23,16 @@
 //    touches those slots, so the main loop has no barriers: a wave only
 //    waits for its own copies.
 //  * v_mfma_i32_16x16x64_i8 with the weights as the first operand: lane l
-//    supplies row l % 16 and bytes 16 (l / 16) .. + 15 of the 64-byte stage
-//    of both operands (the same k for both, which is all the product needs),
-//    and receives token l % 16 of rows 4 (l / 16) .. + 3 of the block.  In
-//    LDS a stage's 16-row block is 1 KiB, 64 bytes a row, with 16-byte
-//    segment s of row r at s ^ ((r >> 2) & 3), so the eight rows one LDS
-//    read cycle serves hit distinct banks.
+//    supplies row l % 16 and 16-byte segment g' of the 64-byte stage of both
+//    operands, g' = 0, 3, 1, 2 for l / 16 = 0 .. 3 (the same k for both,
+//    which is all the product needs), and receives token l % 16 of rows
+//    4 (l / 16) .. + 3 of the block.  In LDS a stage's 16-row block is 1 KiB,
+//    64 bytes a row, with segment s of row r at s ^ ((r >> 2) & 3).  A
+//    16-byte LDS read serves 16 lanes a cycle: per half-wave, those whose
+//    4-lane quad index (lane bits 2-4) has one parity, as the LDS
+//    bank-conflict counter shows -- rows 0-3 and 12-15 of one lane group and
+//    rows 4-11 of the next.  Segments that differ by 3 between those two
+//    groups put the 16 reads in distinct banks.
 //  * At the end of a pass the four waves' int32 partial sums meet in LDS
 //    (exact integer adds); each wave finishes a quarter of the blocks with the
 //    same rescale as the tiled GEMM, so the fp16 outputs equal the tiled
@@ -78,9 +82,10 @@ void gemm_skinny_kernel(GemmArgs args, int units, int i32_out)
     // i.e. the logical segment the swizzle puts there (an involution)
     const int crow = lane >> 2;
     const uint32_t co = (uint32_t)(crow * K + 16 * ((lane & 3) ^ ((crow >> 2) & 3)));
-    // fragments: lane l reads row l%16, logical segment l/16
+    // fragments: lane l reads row l%16, logical segment g' (l/16 = g: 0, 3, 1, 2)
     const int frow = lane & 15;
-    const int fo = frow * 64 + 16 * ((lane >> 4) ^ ((frow >> 2) & 3));
+    const int fseg = (3 * ((lane >> 4) & 1)) ^ (lane >> 5);
+    const int fo = frow * 64 + 16 * (fseg ^ ((frow >> 2) & 3));
     const v4i rx = make_rsrc(args.xq, (uint32_t)(M * K));
     int8_t *const wl = lds + wave * WAVE_LDS;
 
