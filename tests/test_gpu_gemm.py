@@ -75,6 +75,9 @@ PC_SHAPES = [
     # per wave), N = 129 (most workgroups have no rows)
     (33, 10240, 2560), (47, 10243, 384), (77, 3001, 1280), (128, 8192, 4096),
     (200, 1030, 8192), (256, 2000, 8192), (40, 129, 256),
+    # ... up to 256 tokens at N <= 5120 (two slices of 80, N ragged), and
+    # 65-127 tokens up to N = 10240 (two slices of 56)
+    (160, 4100, 1280), (112, 10000, 640),
 ]
 
 
@@ -117,6 +120,9 @@ EXPECTED_TILES = {
     (200, 1030, 8192): (128, 16, 4),       # two slices of 100 tokens
     (256, 2000, 8192): (128, 16, 4),
     (40, 129, 256): (64, 16, 4),
+    (160, 4100, 1280): (128, 48, 4),       # two slices of 80 tokens, 40 rows
+    (112, 10000, 640): (64, 80, 4),        # two slices of 56 tokens, 80 rows
+    (96, 14336, 4096): (64, 128, 4),       # 65-127 tokens beyond N = 10240: tiles
 }
 
 

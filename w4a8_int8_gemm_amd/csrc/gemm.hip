@@ -984,9 +984,16 @@ TileShape choose_tile(GemmMode mode, int gs, int M, int N, int K, int num_cu)
     // tokens: 128x8192x4096 13.8 against 15.1 us, 100x4096x14336 26 against
     // 30 us, against the K-split form below), and for long rows (K >= 8192, up
     // to 256 tokens: 256x4096x14336 36 against 39 us, 43 against 54 us with
-    // the weights from HBM).  At N=10240, K=2560 from 64 tokens on the tiles
-    // win (128 tokens: 10.0 against 12.3 us).
-    if (!pergroup && M > 32 && M <= 256 && (M <= 48 || K >= 8192 || (M <= 128 && N <= 8192)) &&
+    // the weights from HBM), for outputs up to 5120 wide up to 256 tokens
+    // (256x2048x4096 9.7 against 13.5 us, 200x4096x4096 11.3 against 14.9,
+    // 200x5120x4096 14.2 against 15.0), and between 64 and 128 tokens up to
+    // N = 10240, where the tiles of 128 tokens run part empty (112x10240x2560
+    // 10.8 against 12.1 us).  The tiles win at 64 and 128 tokens at N=10240,
+    // K=2560 (128: 10.0 against 11.0 us) and from 64 tokens at N=14336,
+    // K=4096 (96: 15.7 against 17.1 us).
+    if (!pergroup && M > 32 && M <= 256 &&
+        (M <= 48 || K >= 8192 || N <= 5120 || (M <= 128 && N <= 8192) ||
+         (M > 64 && M < 128 && N <= 10240)) &&
         plan_gemm_rows(M, N, K, num_cu).ok)
         return TileShape::TRows;
     // Few tokens per channel: the product is bound by one pass over the
