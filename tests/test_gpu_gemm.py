@@ -108,8 +108,8 @@ EXPECTED_TILES = {
     (7, 5, 64): (16, 16, 4),
     (24, 40000, 192): (32, 128, 4),        # 160 rows per workgroup: two passes
     (65, 6150, 320): (128, 32, 4),         # K % 128 != 0: not the shared-stage form
-    (64, 10240, 2560): (64, 64, 2),        # 49-256 tokens with N > 8192 and K < 8192: tiles
-    (128, 10240, 2560): (64, 128, 4),
+    (64, 10240, 2560): (64, 48, 4),        # one slice, 40 rows per workgroup
+    (128, 10240, 2560): (64, 80, 4),       # two slices of 64 tokens, 80 rows
     # 33-256 tokens, the row-range form with shared stages (the tokens of a
     # slice padded to 64 per block per wave, the rows of a range padded to 16)
     (33, 10240, 2560): (64, 48, 4),        # one slice, 40 rows per workgroup
@@ -122,7 +122,7 @@ EXPECTED_TILES = {
     (40, 129, 256): (64, 16, 4),
     (160, 4100, 1280): (128, 48, 4),       # two slices of 80 tokens, 40 rows
     (112, 10000, 640): (64, 80, 4),        # two slices of 56 tokens, 80 rows
-    (96, 14336, 4096): (64, 128, 4),       # 65-127 tokens beyond N = 10240: tiles
+    (96, 14336, 4096): (128, 64, 4),       # one slice (two blocks of 16 per wave), 56 rows
 }
 
 

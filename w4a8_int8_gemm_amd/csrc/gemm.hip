@@ -978,23 +978,14 @@ TileShape choose_tile(GemmMode mode, int gs, int M, int N, int K, int num_cu)
     const int64_t t128x128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
     // Tens to hundreds of tokens per channel: the product is bound by moving
     // bytes.  The row-range form with shared stages (one compute unit per
-    // weight-row range and token slice) measured faster than the alternatives
-    // for 33-48 tokens (N=10240, K=2560: 9.4 against 10.5 us on 64x64 tiles),
-    // where the output is too narrow for enough tiles (N <= 8192, up to 128
-    // tokens: 128x8192x4096 13.8 against 15.1 us, 100x4096x14336 26 against
-    // 30 us, against the K-split form below), and for long rows (K >= 8192, up
-    // to 256 tokens: 256x4096x14336 36 against 39 us, 43 against 54 us with
-    // the weights from HBM), for outputs up to 5120 wide up to 256 tokens
-    // (256x2048x4096 9.7 against 13.5 us, 200x4096x4096 11.3 against 14.9,
-    // 200x5120x4096 14.2 against 15.0), and between 64 and 128 tokens up to
-    // N = 10240, where the tiles of 128 tokens run part empty (112x10240x2560
-    // 10.8 against 12.1 us).  The tiles win at 64 and 128 tokens at N=10240,
-    // K=2560 (128: 10.0 against 11.0 us) and from 64 tokens at N=14336,
-    // K=4096 (96: 15.7 against 17.1 us).
-    if (!pergroup && M > 32 && M <= 256 &&
-        (M <= 48 || K >= 8192 || N <= 5120 || (M <= 128 && N <= 8192) ||
-         (M > 64 && M < 128 && N <= 10240)) &&
-        plan_gemm_rows(M, N, K, num_cu).ok)
+    // weight-row range and token slice) measured faster than the tiles for
+    // 33-256 tokens wherever it applies (K % 128 == 0), warm and with the
+    // weights from HBM (warm / cold us against the tiles: 64x10240x2560
+    // 7.7 / 8.8 against 9.3 / 10.4, 128x10240x2560 9.7 / 10.3 against
+    // 9.9 / 13.2, 256x10240x2560 13.1 / 16.3 against 13.9 / 21.8,
+    // 128x14336x4096 15.3 / 19.6 against 15.9 / 20.4, 256x4096x14336 29.2
+    // against 39).
+    if (!pergroup && M > 32 && M <= 256 && plan_gemm_rows(M, N, K, num_cu).ok)
         return TileShape::TRows;
     // Few tokens per channel: the product is bound by one pass over the
     // weights, and the row-range form that splits K over its waves (each

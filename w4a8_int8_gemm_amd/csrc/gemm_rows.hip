@@ -181,6 +181,26 @@ void gemm_rows_kernel(GemmArgs args, int units, int pm_slices, int i32_out)
     // stage s+1's fragments and computes stage s from the fragments read in
     // the previous iteration, so the LDS reads run beside the MFMAs.
     static_assert(D >= 3, "ring depth");
+    // The epilogue's scales are loaded first, so that they arrive with the
+    // first stage instead of costing a round trip after the last one.
+    // Indices are clamped to the arrays; the int32 export has no scales and
+    // reads (and ignores) the leading bytes of its operands instead.
+    const float *const sa_src = i32_out ? reinterpret_cast<const float *>(args.xq) : args.sa;
+    const float *const sw_src = i32_out ? static_cast<const float *>(args.w) : args.sw;
+    float sa_pre[MBW], sw_pre[RB][4];
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+        const int m = m_begin + (wave * MBW + mb) * 16 + (lane & 15);
+        sa_pre[mb] = sa_src[i32_out ? 0 : min(m, M - 1)];
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int n = r_begin + rb * 16 + 4 * (lane >> 4) + r;
+            sw_pre[rb][r] = sw_src[i32_out ? 0 : min(n, N - 1)];
+        }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < D - 1; ++t)
         issue_stage(t, t);
@@ -217,7 +237,7 @@ void gemm_rows_kernel(GemmArgs args, int units, int pm_slices, int i32_out)
         const int m = m_begin + (wave * MBW + mb) * 16 + (lane & 15);
         if (m >= m_end)
             continue;
-        const float sam = i32_out ? 0.0f : args.sa[m];
+        const float sam = sa_pre[mb];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int n = r_begin + rb * 16 + 4 * (lane >> 4);
@@ -240,7 +260,7 @@ void gemm_rows_kernel(GemmArgs args, int units, int pm_slices, int i32_out)
                 uint16_t h[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[r] = (n + r < r_end) ? f2h(rescale_pc(s[r], sam, args.sw[n + r])) : (uint16_t)0;
+                    h[r] = (n + r < r_end) ? f2h(rescale_pc(s[r], sam, sw_pre[rb][r])) : (uint16_t)0;
                 if (whole && (N & 3) == 0 && ((uintptr_t)args.out & 7) == 0) {
                     *reinterpret_cast<uint2 *>(Y) =
                         make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),

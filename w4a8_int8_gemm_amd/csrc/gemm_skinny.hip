@@ -103,6 +103,28 @@ void gemm_skinny_kernel(GemmArgs args, int units, int i32_out)
             for (int mb = 0; mb < MB; ++mb)
                 acc[rb][mb] = v4i{0, 0, 0, 0};
 
+        // The scales of the blocks this wave finishes (blocks wave, wave + 4,
+        // ...), loaded before the pass's copies so that they arrive with the
+        // first stage instead of costing a round trip at the end.  Indices
+        // are clamped to the arrays; the int32 export has no scales and reads
+        // (and ignores) the leading bytes of its operands instead.
+        constexpr int NBW = (RB * MB + SKW - 1) / SKW;
+        const float *const sa_src = i32_out ? reinterpret_cast<const float *>(args.xq) : args.sa;
+        const float *const sw_src = i32_out ? static_cast<const float *>(args.w) : args.sw;
+        float sa_pre[NBW], sw_pre[NBW][4];
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            const int b = min(wave + SKW * i, RB * MB - 1);
+            const int rb = b / MB, mb = b % MB;
+            const int m = mb * 16 + (lane & 15);
+            const int n = p0 + rb * 16 + 4 * (lane >> 4);
+            sa_pre[i] = sa_src[i32_out ? 0 : min(m, M - 1)];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sw_pre[i][r] = sw_src[i32_out ? 0 : min(n + r, N - 1)];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
         // Stage t of this wave (unit wave + 4 t, rotated) into slot d.
         auto copy = [&](int d, int t) __attribute__((always_inline)) {
             int u = wave + SKW * t + rot;
@@ -174,8 +196,11 @@ void gemm_skinny_kernel(GemmArgs args, int units, int i32_out)
             for (int mb = 0; mb < MB; ++mb)
                 red[((wave * RB + rb) * MB + mb) * 64 + lane] = acc[rb][mb];
         lds_barrier();
-#pragma unroll 1
-        for (int b = wave; b < RB * MB; b += SKW) {
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) {
+            const int b = wave + SKW * i;
+            if (b >= RB * MB)
+                break;
             const int rb = b / MB, mb = b % MB;
             v4i s = red[b * 64 + lane];
 #pragma unroll
@@ -200,11 +225,11 @@ void gemm_skinny_kernel(GemmArgs args, int units, int i32_out)
                 }
             } else {
                 uint16_t *Y = static_cast<uint16_t *>(args.out) + (int64_t)m * N + n;
-                const float sam = args.sa[m];
+                const float sam = sa_pre[i];
                 uint16_t h[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[r] = (n + r < r_end) ? f2h(rescale_pc(s[r], sam, args.sw[n + r])) : (uint16_t)0;
+                    h[r] = (n + r < r_end) ? f2h(rescale_pc(s[r], sam, sw_pre[i][r])) : (uint16_t)0;
                 if (whole && (N & 3) == 0 && ((uintptr_t)args.out & 7) == 0) {
                     *reinterpret_cast<uint2 *>(Y) =
                         make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
