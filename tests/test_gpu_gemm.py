@@ -76,8 +76,10 @@ PC_SHAPES = [
     (33, 10240, 2560), (47, 10243, 384), (77, 3001, 1280), (128, 8192, 4096),
     (200, 1030, 8192), (256, 2000, 8192), (40, 129, 256),
     # ... up to 256 tokens at N <= 5120 (two slices of 80, N ragged), and
-    # 65-127 tokens up to N = 10240 (two slices of 56)
-    (160, 4100, 1280), (112, 10000, 640),
+    # 65-127 tokens up to N = 10240 (two slices of 56); wide outputs: one
+    # slice of two token blocks per wave (N=14336), eight row blocks of 16
+    # per range (N ragged against the 8-row units)
+    (160, 4100, 1280), (112, 10000, 640), (96, 14336, 1024), (200, 16380, 256),
 ]
 
 
@@ -123,6 +125,8 @@ EXPECTED_TILES = {
     (160, 4100, 1280): (128, 48, 4),       # two slices of 80 tokens, 40 rows
     (112, 10000, 640): (64, 80, 4),        # two slices of 56 tokens, 80 rows
     (96, 14336, 4096): (128, 64, 4),       # one slice (two blocks of 16 per wave), 56 rows
+    (96, 14336, 1024): (128, 64, 4),
+    (200, 16380, 256): (128, 128, 4),      # two slices of 100 tokens, 128 rows
 }
 
 
