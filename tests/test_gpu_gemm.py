@@ -80,6 +80,7 @@ PC_SHAPES = [
     # slice of two token blocks per wave (N=14336), eight row blocks of 16
     # per range (N ragged against the 8-row units)
     (160, 4100, 1280), (112, 10000, 640), (96, 14336, 1024), (200, 16380, 256),
+    (120, 30000, 256),
 ]
 
 
@@ -127,6 +128,7 @@ EXPECTED_TILES = {
     (96, 14336, 4096): (128, 64, 4),       # one slice (two blocks of 16 per wave), 56 rows
     (96, 14336, 1024): (128, 64, 4),
     (200, 16380, 256): (128, 128, 4),      # two slices of 100 tokens, 128 rows
+    (120, 30000, 256): (128, 128, 4),      # one slice, 120 rows of 30000 / 256 ranges
 }
 
 
